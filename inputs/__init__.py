@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the fused FP8 MoE layer (one GPU's expert-parallel share).
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the benchmark.
+It holds shapes and random draws only: none of the layer's arithmetic (routing, pooling,
+GEMMs, SwiGLU, requantisation, combine) lives here.  Inputs are quantised to FP8 e4m3fn
+with torch's own dtype cast, which plays the role of the upstream model that hands the
+layer FP8 activations and block-scaled FP8 weights.
+
+Input recipe (the workload descriptions the layer is quoted on):
+  * x ~ N(0, 1) of shape [S, T, H], quantised per token and per 128 columns:
+    scale = amax / 448, codes = e4m3fn(x / scale).
+  * W1 ~ N(0, 0.02^2) of shape [E_l, 2I, H] (rows 0..I-1 gate, I..2I-1 up) and
+    W2 ~ N(0, 0.02^2) of shape [E_l, H, I], quantised per 128x128 block the same way.
+  * topk_idx: K distinct experts per token.  "uniform": a uniformly random K-subset.
+    "zipf": expert at rank j of a seeded permutation has weight j^-alpha and K experts are
+    drawn without replacement (Gumbel top-k, i.e. successive draws proportional to weight).
+  * topk_weights = softmax of N(0, 1) logits over the K chosen experts.
+Draw order is fixed: x, W1, W2, routing keys, logits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence
+
+import torch
+
+FP8_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class MoEShape:
+    """Shape of one GPU's share of an expert-parallel MoE layer.
+
+    Source ranks are emulated as ``num_shards`` token shards resident on the one GPU.
+    This GPU owns global experts [local_rank*E_l, (local_rank+1)*E_l).
+    """
+    name: str
+    num_shards: int            # S
+    max_tokens_per_shard: int  # T_max
+    hidden: int                # H
+    intermediate: int          # I
+    num_experts: int           # E (global)
+    num_local_experts: int     # E_l
+    topk: int                  # K
+    block_m: int               # BLOCK_M of the expert pool
+    local_rank: int = 0
+    routing: str = "uniform"   # "uniform" | "zipf"
+    zipf_alpha: float = 1.2
+    seed: int = 0
+
+    def replace(self, **kw) -> "MoEShape":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads.  Seeds: tiny 0, decode 1, prefill 2, skewed 3, mid 4.
+SHAPES: Dict[str, MoEShape] = {
+    "tiny": MoEShape("tiny", 1, 64, 256, 512, 8, 8, 2, 64, seed=0),
+    "decode": MoEShape("decode", 8, 128, 7168, 2048, 256, 32, 8, 64, seed=1),
+    "prefill": MoEShape("prefill", 8, 4096, 7168, 2048, 256, 32, 8, 128, seed=2),
+    "skewed": MoEShape("skewed", 8, 2048, 7168, 2048, 256, 32, 8, 128,
+                       routing="zipf", zipf_alpha=1.2, seed=3),
+    "mid": MoEShape("mid", 4, 1024, 4096, 1536, 128, 32, 8, 128, seed=4),
+}
+
+
+def _quant_rows_per128(x: torch.Tensor):
+    """[..., C] float32 -> (uint8 e4m3fn codes [..., C], float32 scales [..., C/128])."""
+    *lead, c = x.shape
+    xb = x.reshape(*lead, c // 128, 128)
+    amax = xb.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    q = (xb / scale.unsqueeze(-1)).to(torch.float8_e4m3fn)
+    return q.reshape(*lead, c).view(torch.uint8), scale.to(torch.float32)
+
+
+def _quant_block128(w: torch.Tensor):
+    """[N, C] float32 -> (uint8 codes [N, C], float32 scales [N/128, C/128])."""
+    n, c = w.shape
+    wb = w.reshape(n // 128, 128, c // 128, 128)
+    amax = wb.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    q = (wb / scale[:, None, :, None]).to(torch.float8_e4m3fn)
+    return q.reshape(n, c).view(torch.uint8), scale.to(torch.float32)
+
+
+def _route(shape: MoEShape, gen: torch.Generator, device) -> torch.Tensor:
+    S, T, E, K = shape.num_shards, shape.max_tokens_per_shard, shape.num_experts, shape.topk
+    if shape.routing == "uniform":
+        keys = torch.rand((S, T, E), generator=gen, device=device)
+    elif shape.routing == "zipf":
+        perm = torch.randperm(E, generator=gen, device=device)
+        rank_w = torch.arange(1, E + 1, device=device, dtype=torch.float64).pow(-shape.zipf_alpha)
+        logp = torch.empty(E, dtype=torch.float64, device=device)
+        logp[perm] = rank_w.log()
+        u = torch.rand((S, T, E), generator=gen, device=device, dtype=torch.float64)
+        u = u.clamp_min(1e-300)
+        keys = logp - torch.log(-torch.log(u))
+    else:
+        raise ValueError(f"unknown routing {shape.routing!r}")
+    return keys.topk(K, dim=-1).indices.to(torch.int64)
+
+
+def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
+                tokens_per_shard: Optional[Sequence[int]] = None,
+                integer_codes: bool = False) -> Dict[str, object]:
+    """Draw one seeded input set.  Returns a dict of tensors on ``device``:
+
+    x [S,T,H] u8 (e4m3fn codes), x_sf [S,T,H/128] f32, topk_idx [S,T,K] i64,
+    topk_weights [S,T,K] f32, w1 [E_l,2I,H] u8, w1_sf [E_l,2I/128,H/128] f32,
+    w2 [E_l,H,I] u8, w2_sf [E_l,H/128,I/128] f32, and tokens_per_shard (list of int).
+
+    integer_codes=True draws every FP8 code from the integers -8..8 and every scale as
+    one shared power of two (2^-4 for activations, 2^-6 for weights), so that every
+    product and every partial sum of the GEMMs is exact in fp32.
+    """
+    S, T, H, I = shape.num_shards, shape.max_tokens_per_shard, shape.hidden, shape.intermediate
+    El, K = shape.num_local_experts, shape.topk
+    if H % 128 or I % 128:
+        raise ValueError("hidden and intermediate must be multiples of 128")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(shape.seed if seed is None else seed)
+
+    def ints(shape_):
+        v = torch.randint(-8, 9, shape_, generator=gen, device=device).to(torch.float32)
+        return v.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    if integer_codes:
+        x = ints((S, T, H))
+        x_sf = torch.full((S, T, H // 128), 2.0 ** -4, device=device)
+        w1 = ints((El, 2 * I, H))
+        w1_sf = torch.full((El, 2 * I // 128, H // 128), 2.0 ** -6, device=device)
+        w2 = ints((El, H, I))
+        w2_sf = torch.full((El, H // 128, I // 128), 2.0 ** -6, device=device)
+    else:
+        x, x_sf = _quant_rows_per128(torch.randn((S, T, H), generator=gen, device=device))
+        w1 = torch.empty((El, 2 * I, H), dtype=torch.uint8, device=device)
+        w1_sf = torch.empty((El, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
+        for e in range(El):
+            w = torch.randn((2 * I, H), generator=gen, device=device) * 0.02
+            w1[e], w1_sf[e] = _quant_block128(w)
+        w2 = torch.empty((El, H, I), dtype=torch.uint8, device=device)
+        w2_sf = torch.empty((El, H // 128, I // 128), dtype=torch.float32, device=device)
+        for e in range(El):
+            w = torch.randn((H, I), generator=gen, device=device) * 0.02
+            w2[e], w2_sf[e] = _quant_block128(w)
+    topk_idx = _route(shape, gen, device)
+    logits = torch.randn((S, T, K), generator=gen, device=device)
+    topk_weights = torch.softmax(logits, dim=-1).to(torch.float32)
+    if tokens_per_shard is None:
+        tokens_per_shard = [T] * S
+    tokens_per_shard = [int(t) for t in tokens_per_shard]
+    if len(tokens_per_shard) != S or any(t < 0 or t > T for t in tokens_per_shard):
+        raise ValueError("tokens_per_shard must hold S values in [0, T_max]")
+    return dict(x=x, x_sf=x_sf, topk_idx=topk_idx, topk_weights=topk_weights,
+                w1=w1, w1_sf=w1_sf, w2=w2, w2_sf=w2_sf, tokens_per_shard=tokens_per_shard)
+
+
+def to_numpy(inputs: Dict[str, object]) -> Dict[str, object]:
+    """Host (numpy) copies of an input set, for the CPU oracle."""
+    out = {}
+    for k, v in inputs.items():
+        out[k] = v.detach().cpu().numpy() if isinstance(v, torch.Tensor) else v
+    return out
+
+
+def digest(inputs: Dict[str, object]) -> str:
+    """Short content hash of an input set (recorded next to results)."""
+    h = hashlib.sha256()
+    for k in sorted(inputs):
+        v = inputs[k]
+        if isinstance(v, torch.Tensor):
+            h.update(k.encode())
+            h.update(v.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
+        else:
+            h.update(repr((k, v)).encode())
+    return h.hexdigest()[:16]
