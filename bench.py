@@ -1,0 +1,173 @@
+"""Benchmark of the fused FP8 MoE layer on one MI355X: routed tokens/s and GEMM % of FP8 MFMA peak.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill] [--no-cpu-baseline]
+
+One step = one mega_moe_forward (routing, pool fill, GEMM1 + SwiGLU + requant, GEMM2 + scatter,
+combine) over one resident batch of seeded synthetic inputs.  The timed region brackets exactly
+`steps` forwards with a device synchronisation on both sides; inputs and weights are already in HBM.
+Per-stage times come from HIP events the library records on the forward's stream inside the timed
+region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+WORKLOAD_TEXT = {
+    "prefill": "prefill-shaped EP=8 share: 8 shards x 4096 tokens, H=7168, I=2048, 32 of 256 experts local, "
+               "top-8 uniform, FP8 e4m3 (per-128 activation scales, 128x128 weight scales), BLOCK_M=128",
+    "decode": "decode-shaped EP=8 share: 8 shards x 128 tokens, H=7168, I=2048, 32 of 256 experts local, "
+              "top-8 uniform, BLOCK_M=64",
+    "skewed": "skewed EP=8 share: 8 shards x 2048 tokens, H=7168, I=2048, 32 of 256 experts local, "
+              "top-8 Zipf(1.2), BLOCK_M=128",
+    "mid": "mid-size MoE: 4 shards x 1024 tokens, H=4096, I=1536, 32 of 128 experts local, top-8, BLOCK_M=128",
+    "tiny": "tiny: 1 shard x 64 tokens, H=256, I=512, 8 experts all local, top-2, BLOCK_M=64",
+}
+
+
+def algorithmic(shape, R, N):
+    """Algorithmic work per forward (valid routed rows only, no padding)."""
+    H, I, K = shape.hidden, shape.intermediate, shape.topk
+    El = shape.num_local_experts
+    return dict(
+        gemm1_flop=4.0 * R * H * I,
+        gemm2_flop=2.0 * R * I * H,
+        # route: read every (token, k) expert id, write one table entry per routed pair
+        route_bytes=N * K * 8 + R * 4,
+        # fill: read the row and its scales, write them and 12 B of metadata, read the table entry
+        fill_bytes=R * (2 * H + 2 * (H // 128) * 4 + 12 + 4),
+        # combine: read each routed pair's bf16 row, read K ids + weights per token, write the bf16 row
+        combine_bytes=R * 2 * H + N * (2 * H + K * 12),
+        weight_bytes=El * 3 * H * I + El * (2 * I // 128) * (H // 128) * 4 + El * (H // 128) * (I // 128) * 4,
+    )
+
+
+def cpu_baseline(shape, inp_gpu, n_experts: int):
+    """The CPU oracle, as is, on a bounded sample of the same workload: the whole routing and pool
+    fill, then the FFN of the first n_experts local experts.  Rate = their routed rows / seconds."""
+    import oracle
+    import threadpoolctl
+    from inputs import to_numpy
+    inp = to_numpy(inp_gpu)
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    out = oracle.forward(inp, shape.num_experts, shape.num_local_experts, shape.local_rank, shape.block_m,
+                         experts=list(range(n_experts)))
+    dt = time.perf_counter() - t0
+    rows = int(out["route"].recv_tot[:n_experts].sum())
+    return {"value": rows / dt, "unit": "routed tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{shape.name} workload: routing and pool fill of all {int(out['route'].recv_tot.sum())} "
+                      f"routed rows, FFN + combine of local experts 0..{n_experts - 1} ({rows} rows), "
+                      f"numpy fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's expert-parallel share; --gpus {args.gpus} is not supported "
+              f"(source ranks are emulated as shards on the one GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dispatch_fp8_grouped_amd as mm
+    from inputs import SHAPES, make_inputs
+
+    shape = SHAPES[args.workload]
+    torch.cuda.set_device(0)
+    inp = make_inputs(shape, device="cuda")
+    moe = mm.MegaMoE.from_shape(shape)
+    y = torch.empty((shape.num_shards, shape.max_tokens_per_shard, shape.hidden), dtype=torch.bfloat16,
+                    device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe(inp, y=y)
+    torch.cuda.synchronize()
+    status = moe.status()
+    if status:
+        raise SystemExit(f"device status {status:#x} after warmup")
+    recv_tot = moe.region("recv_tot", torch.int32, (shape.num_local_experts,)).cpu()
+    R = int(recv_tot.sum())
+    N = sum(inp["tokens_per_shard"])
+
+    mm.mega_moe_set_timing(moe.h, True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        moe(inp, y=y)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    stage_ms, nt = mm.mega_moe_stage_times(moe.h, with_count=True)
+    mm.mega_moe_set_timing(moe.h, False)
+    assert nt == args.steps
+    ms = ms_total / args.steps
+    status = moe.status()
+    if status:
+        raise SystemExit(f"device status {status:#x} after the timed steps")
+
+    w = algorithmic(shape, R, N)
+    st = dict(zip(mm.STAGE_NAMES, stage_ms))
+    g1_tflops = w["gemm1_flop"] / (st["gemm1"] * 1e-3) / 1e12
+    g2_tflops = w["gemm2_flop"] / (st["gemm2"] * 1e-3) / 1e12
+    gemm_tflops = (w["gemm1_flop"] + w["gemm2_flop"]) / ((st["gemm1"] + st["gemm2"]) * 1e-3) / 1e12
+    gbs = lambda b, t: b / (t * 1e-3) / 1e9  # noqa: E731
+    out = {
+        "metric": "routed tokens/s of fused MoE layer at 1 GPU; GEMM % of FP8 MFMA peak",
+        "value": R / (ms * 1e-3),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "routed_rows": R, "tokens": N,
+                   "parallelism": "one GPU's EP share, source ranks emulated as shards"},
+        "gemm_pct_fp8_peak": 100.0 * gemm_tflops / FP8_PEAK_TFLOPS,
+        "gemm_tflops": gemm_tflops,
+        "roofline": {"bound": "mfma", "kernel": "gemm1 (gate_up + SwiGLU + requant)",
+                     "achieved": g1_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": g1_tflops / FP8_PEAK_TFLOPS, "traffic": None},
+        "stages_ms": st,
+        "stages": {
+            "route": {"GB/s": gbs(w["route_bytes"], st["route"])},
+            "fill": {"GB/s": gbs(w["fill_bytes"], st["fill"]),
+                     "hbm_frac": gbs(w["fill_bytes"], st["fill"]) / HBM_PEAK_GBS},
+            "gemm1": {"TFLOP/s": g1_tflops, "frac": g1_tflops / FP8_PEAK_TFLOPS},
+            "gemm2": {"TFLOP/s": g2_tflops, "frac": g2_tflops / FP8_PEAK_TFLOPS},
+            "combine": {"GB/s": gbs(w["combine_bytes"], st["combine"]),
+                        "hbm_frac": gbs(w["combine_bytes"], st["combine"]) / HBM_PEAK_GBS},
+            "weights_stream_GB/s": gbs(w["weight_bytes"], st["gemm1"] + st["gemm2"]),
+        },
+    }
+    moe.close()
+    if not args.no_cpu_baseline:
+        n_exp = min(args.cpu_experts, shape.num_local_experts)
+        out["cpu_baseline"] = cpu_baseline(shape, inp, n_exp)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,356 @@
+// Host side of libmegamoe: argument checks, workspace layout, stage launches, status and timing.
+//
+// The setup mirrors the pages' buffer handling ("DeepGEMM Mega MoE symmetric memory deep analysis",
+// 4.1-4.2 and 5.1): the caller asks for a size, allocates one block of device memory and hands it
+// over; the library carves it into fixed regions.  Pool capacity follows the same page's bound
+// (4.2): ceil(max routed rows / BLOCK_M) + E_l blocks.  There is no cross-GPU symmetric memory here:
+// the S source shards live in this GPU's HBM, so every pointer is local.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "mm_internal.h"
+
+using mm::Params;
+
+static constexpr int kTimingSets = 64;
+
+struct mega_moe_handle {
+    mega_moe_config cfg;
+    mega_moe_layout lay;
+    uint8_t* ws;
+    uint64_t ws_bytes;
+    int device;
+    int num_cus;
+    // stage timing: a ring of event sets, folded into running sums when a set is reused
+    bool timing;
+    int next_set;                                   // forwards recorded since the reset
+    hipEvent_t ev[kTimingSets][MEGA_MOE_NUM_STAGES + 1];
+    uint32_t ran[kTimingSets];
+    bool pending[kTimingSets];
+    double sum_ms[MEGA_MOE_NUM_STAGES];
+    int runs[MEGA_MOE_NUM_STAGES];
+};
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int32_t check_config(const mega_moe_config* c) {
+    if (!c) return MEGA_MOE_ERR_INVALID_ARG;
+    if (c->num_shards < 1 || c->num_shards > MEGA_MOE_MAX_SHARDS) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->max_tokens_per_shard < 1) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->hidden < 256 || c->hidden > 16384 || c->hidden % 256 != 0) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->intermediate < 128 || c->intermediate > 16384 || c->intermediate % 128 != 0)
+        return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->num_local_experts < 1 || c->num_local_experts > MEGA_MOE_MAX_LOCAL_EXPERTS)
+        return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->num_experts < 1 || c->num_experts > MEGA_MOE_MAX_EXPERTS ||
+        c->num_experts % c->num_local_experts != 0)
+        return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->local_rank < 0 || c->local_rank >= c->num_experts / c->num_local_experts)
+        return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->topk < 1 || c->topk > MEGA_MOE_MAX_TOPK) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->block_m != 0 && c->block_m != 64 && c->block_m != 128) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->flags & ~MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) return MEGA_MOE_ERR_UNSUPPORTED;
+    // table entries are int32 t*K+k
+    if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
+    return MEGA_MOE_OK;
+}
+
+int resolve_block_m(const mega_moe_config* c) {
+    if (c->block_m) return c->block_m;
+    // expected rows per local expert under uniform routing: S*T_max*K/E
+    const double rows = (double)c->num_shards * c->max_tokens_per_shard * c->topk / c->num_experts;
+    return rows <= 64.0 ? 64 : 128;
+}
+
+void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
+    memset(L, 0, sizeof(*L));
+    const uint64_t S = c->num_shards, T = c->max_tokens_per_shard, H = c->hidden, I = c->intermediate;
+    const uint64_t E = c->num_experts, El = c->num_local_experts, K = c->topk;
+    const int bm = resolve_block_m(c);
+    const uint64_t chunks = (T * K + mm::kRouteChunk - 1) / mm::kRouteChunk;
+    const uint64_t kloc = K < El ? K : El;
+    const uint64_t max_routed = S * T * kloc;
+    const uint64_t max_blocks = (max_routed + bm - 1) / bm + El;
+    const uint64_t rows = max_blocks * bm;
+    L->block_m = bm;
+    L->route_chunks = (int32_t)chunks;
+    L->max_pool_blocks = (int32_t)max_blocks;
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) { const uint64_t at = o; o = align_up(o + bytes); return at; };
+    L->status = take(kAlign);
+    L->chunk_hist = take(S * chunks * E * 4);
+    L->chunk_base = take(S * chunks * El * 4);
+    L->send = take(S * E * 4);
+    L->recv = take(El * S * 4);
+    L->recv_tot = take(El * 4);
+    L->pool_off = take((El + 1) * 4);
+    L->block_expert = take(max_blocks * 4);
+    L->block_index = take(max_blocks * 4);
+    L->table = take(El * S * T * 4);
+    L->pool_x = take(rows * H);
+    L->pool_sf = take(rows * (H / 128) * 4);
+    L->pool_meta = take(rows * 3 * 4);
+    L->l2_x = take(rows * I);
+    L->l2_sf = take(rows * (I / 128) * 4);
+    L->comb = take(K * S * T * H * 2);
+    L->gemm1_out = (c->flags & MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) ? take(rows * 2 * I * 4) : 0;
+    L->total = o;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Wait for event set k and add its stage times to the running sums.
+int32_t fold_times(mega_moe_handle* h, int k) {
+    if (hipEventSynchronize(h->ev[k][MEGA_MOE_NUM_STAGES]) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i) {
+        if (!(h->ran[k] & (1u << i))) continue;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, h->ev[k][i], h->ev[k][i + 1]) != hipSuccess) return MEGA_MOE_ERR_HIP;
+        h->sum_ms[i] += t;
+        h->runs[i] += 1;
+    }
+    h->pending[k] = false;
+    return MEGA_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mega_moe_strerror(int32_t code) {
+    switch (code) {
+        case MEGA_MOE_OK: return "ok";
+        case MEGA_MOE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad stage mask)";
+        case MEGA_MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MEGA_MOE_ERR_TOO_MANY_TOKENS: return "tokens_per_shard exceeds max_tokens_per_shard";
+        case MEGA_MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mega_moe_workspace_bytes()";
+        case MEGA_MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error";
+    }
+}
+
+int32_t mega_moe_workspace_bytes(const mega_moe_config* cfg, uint64_t* bytes_out) {
+    if (!cfg || !bytes_out) return MEGA_MOE_ERR_INVALID_ARG;
+    const int32_t rc = check_config(cfg);
+    if (rc) return rc;
+    mega_moe_layout L;
+    make_layout(cfg, &L);
+    *bytes_out = L.total;
+    return MEGA_MOE_OK;
+}
+
+int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t workspace_bytes, void* stream,
+                      mega_moe_handle** out) {
+    if (!cfg || !out) return MEGA_MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    const int32_t rc = check_config(cfg);
+    if (rc) return rc;
+    if (!workspace || !aligned16(workspace) || ((uintptr_t)workspace & (kAlign - 1)))
+        return MEGA_MOE_ERR_INVALID_ARG;
+    mega_moe_layout L;
+    make_layout(cfg, &L);
+    if (workspace_bytes < L.total) return MEGA_MOE_ERR_WORKSPACE_TOO_SMALL;
+    mega_moe_handle* h = new (std::nothrow) mega_moe_handle();
+    if (!h) return MEGA_MOE_ERR_HIP;
+    h->cfg = *cfg;
+    h->lay = L;
+    h->ws = static_cast<uint8_t*>(workspace);
+    h->ws_bytes = workspace_bytes;
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) {
+        delete h;
+        return MEGA_MOE_ERR_HIP;
+    }
+    for (int k = 0; k < kTimingSets; ++k)
+        for (int i = 0; i <= MEGA_MOE_NUM_STAGES; ++i) h->ev[k][i] = nullptr;
+    for (int k = 0; k < kTimingSets; ++k) {
+        for (int i = 0; i <= MEGA_MOE_NUM_STAGES; ++i) {
+            if (hipEventCreate(&h->ev[k][i]) != hipSuccess) {
+                mega_moe_destroy(h);
+                return MEGA_MOE_ERR_HIP;
+            }
+        }
+    }
+    if (hipMemsetAsync(workspace, 0, L.total, static_cast<hipStream_t>(stream)) != hipSuccess) {
+        mega_moe_destroy(h);
+        return MEGA_MOE_ERR_HIP;
+    }
+    *out = h;
+    return MEGA_MOE_OK;
+}
+
+int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32_t* tokens_per_shard,
+                                const void* x, const float* x_sf, const int64_t* topk_idx,
+                                const float* topk_weights, const void* w1, const float* w1_sf, const void* w2,
+                                const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream) {
+    if (!h || !tokens_per_shard) return MEGA_MOE_ERR_INVALID_ARG;
+    if (stages == 0 || (stages & ~MEGA_MOE_STAGE_ALL)) return MEGA_MOE_ERR_INVALID_ARG;
+    const mega_moe_config& c = h->cfg;
+    const bool route = stages & MEGA_MOE_STAGE_ROUTE, fill = stages & MEGA_MOE_STAGE_FILL;
+    const bool g1 = stages & MEGA_MOE_STAGE_GEMM1, g2 = stages & MEGA_MOE_STAGE_GEMM2;
+    const bool comb = stages & MEGA_MOE_STAGE_COMBINE;
+    // pointers each selected stage reads or writes
+    auto need = [](bool used, const void* ptr) { return !used || (ptr && aligned16(ptr)); };
+    if (!need(route || comb, topk_idx) || !need(fill, x) || !need(fill, x_sf) || !need(g1, w1) ||
+        !need(g1, w1_sf) || !need(g2, w2) || !need(g2, w2_sf) || !need(comb, topk_weights) || !need(comb, y))
+        return MEGA_MOE_ERR_INVALID_ARG;
+    if (cum_recv_stats && ((uintptr_t)cum_recv_stats & 3u)) return MEGA_MOE_ERR_INVALID_ARG;
+
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.S = c.num_shards;
+    p.T_max = c.max_tokens_per_shard;
+    p.H = c.hidden;
+    p.I = c.intermediate;
+    p.E = c.num_experts;
+    p.El = c.num_local_experts;
+    p.lo = c.local_rank * c.num_local_experts;
+    p.K = c.topk;
+    p.BM = h->lay.block_m;
+    p.chunks = h->lay.route_chunks;
+    p.max_blocks = h->lay.max_pool_blocks;
+    p.flags = c.flags;
+    for (int s = 0; s < c.num_shards; ++s) {
+        const int32_t t = tokens_per_shard[s];
+        if (t < 0) return MEGA_MOE_ERR_INVALID_ARG;
+        if (t > c.max_tokens_per_shard) return MEGA_MOE_ERR_TOO_MANY_TOKENS;
+        p.tps[s] = t;
+    }
+    const mega_moe_layout& L = h->lay;
+    uint8_t* w = h->ws;
+    p.status = reinterpret_cast<uint32_t*>(w + L.status);
+    p.chunk_hist = reinterpret_cast<int*>(w + L.chunk_hist);
+    p.chunk_base = reinterpret_cast<int*>(w + L.chunk_base);
+    p.send = reinterpret_cast<int*>(w + L.send);
+    p.recv = reinterpret_cast<int*>(w + L.recv);
+    p.recv_tot = reinterpret_cast<int*>(w + L.recv_tot);
+    p.pool_off = reinterpret_cast<int*>(w + L.pool_off);
+    p.block_expert = reinterpret_cast<int*>(w + L.block_expert);
+    p.block_index = reinterpret_cast<int*>(w + L.block_index);
+    p.table = reinterpret_cast<int*>(w + L.table);
+    p.pool_x = w + L.pool_x;
+    p.pool_sf = reinterpret_cast<float*>(w + L.pool_sf);
+    p.pool_meta = reinterpret_cast<uint32_t*>(w + L.pool_meta);
+    p.l2_x = w + L.l2_x;
+    p.l2_sf = reinterpret_cast<float*>(w + L.l2_sf);
+    p.comb = reinterpret_cast<uint16_t*>(w + L.comb);
+    p.gemm1_out = L.gemm1_out ? reinterpret_cast<float*>(w + L.gemm1_out) : nullptr;
+    p.x = static_cast<const uint8_t*>(x);
+    p.x_sf = x_sf;
+    p.topk_idx = topk_idx;
+    p.topk_w = topk_weights;
+    p.w1 = static_cast<const uint8_t*>(w1);
+    p.w1_sf = w1_sf;
+    p.w2 = static_cast<const uint8_t*>(w2);
+    p.w2_sf = w2_sf;
+    p.y = static_cast<uint16_t*>(y);
+    p.cum = cum_recv_stats;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    if (dev != h->device && hipSetDevice(h->device) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t rc = MEGA_MOE_OK;
+    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill, g1, g2, comb};
+    const int set = h->next_set % kTimingSets;
+    if (h->timing && h->pending[set] && fold_times(h, set) != MEGA_MOE_OK) rc = MEGA_MOE_ERR_HIP;
+    uint32_t ran_mask = 0;
+    auto mark = [&](int i) {
+        if (h->timing && !rc && hipEventRecord(h->ev[set][i], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+    };
+    mark(0);
+    for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i) {
+        if (on[i] && !rc) {
+            hipError_t e = hipSuccess;
+            switch (i) {
+                case 0: e = mm::launch_route(p, st); break;
+                case 1: e = mm::launch_fill(p, h->num_cus, st); break;
+                case 2: e = mm::launch_gemm1(p, h->num_cus, st); break;
+                case 3: e = mm::launch_gemm2(p, h->num_cus, st); break;
+                default: e = mm::launch_combine(p, st); break;
+            }
+            if (e != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+            ran_mask |= 1u << i;
+        }
+        mark(i + 1);
+    }
+    if (!rc && h->timing) {
+        h->ran[set] = ran_mask;
+        h->pending[set] = true;
+        ++h->next_set;
+    }
+    if (dev != h->device) (void)hipSetDevice(dev);
+    return rc;
+}
+
+int32_t mega_moe_forward(mega_moe_handle* h, const int32_t* tokens_per_shard, const void* x, const float* x_sf,
+                         const int64_t* topk_idx, const float* topk_weights, const void* w1, const float* w1_sf,
+                         const void* w2, const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream) {
+    return mega_moe_forward_stages(h, MEGA_MOE_STAGE_ALL, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1,
+                                   w1_sf, w2, w2_sf, y, cum_recv_stats, stream);
+}
+
+int32_t mega_moe_query_layout(const mega_moe_handle* h, mega_moe_layout* out) {
+    if (!h || !out) return MEGA_MOE_ERR_INVALID_ARG;
+    *out = h->lay;
+    return MEGA_MOE_OK;
+}
+
+int32_t mega_moe_status(mega_moe_handle* h, void* stream, uint32_t* device_flags) {
+    if (!h || !device_flags) return MEGA_MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    if (hipStreamSynchronize(st) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    if (hipMemcpy(&v, h->ws + h->lay.status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+        return MEGA_MOE_ERR_HIP;
+    if (v) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(h->ws + h->lay.status, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            return MEGA_MOE_ERR_HIP;
+    }
+    *device_flags = v;
+    return MEGA_MOE_OK;
+}
+
+int32_t mega_moe_set_timing(mega_moe_handle* h, int32_t enable) {
+    if (!h) return MEGA_MOE_ERR_INVALID_ARG;
+    // drop whatever was recorded before (waiting for it, so the events can be reused)
+    for (int k = 0; k < kTimingSets; ++k) {
+        if (h->pending[k] && hipEventSynchronize(h->ev[k][MEGA_MOE_NUM_STAGES]) != hipSuccess)
+            return MEGA_MOE_ERR_HIP;
+        h->pending[k] = false;
+    }
+    for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i) {
+        h->sum_ms[i] = 0.0;
+        h->runs[i] = 0;
+    }
+    h->next_set = 0;
+    h->timing = enable != 0;
+    return MEGA_MOE_OK;
+}
+
+int32_t mega_moe_stage_times(mega_moe_handle* h, float* ms, int32_t* count) {
+    if (!h || !ms) return MEGA_MOE_ERR_INVALID_ARG;
+    for (int k = 0; k < kTimingSets; ++k)
+        if (h->pending[k] && fold_times(h, k) != MEGA_MOE_OK) return MEGA_MOE_ERR_HIP;
+    for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i)
+        ms[i] = h->runs[i] ? (float)(h->sum_ms[i] / h->runs[i]) : 0.f;
+    if (count) *count = h->next_set;
+    return MEGA_MOE_OK;
+}
+
+void mega_moe_destroy(mega_moe_handle* h) {
+    if (!h) return;
+    for (int k = 0; k < kTimingSets; ++k)
+        for (int i = 0; i <= MEGA_MOE_NUM_STAGES; ++i)
+            if (h->ev[k][i]) (void)hipEventDestroy(h->ev[k][i]);
+    delete h;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal definitions shared by the HIP translation units of libmegamoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mega_moe.h"
+
+namespace mm {
+
+constexpr int kRouteChunk = 2048;      // flat (token, k) entries per routing work-group
+constexpr int kBK = 128;               // GEMM K step = one scale block
+constexpr int kBN = 256;               // GEMM weight rows per tile
+constexpr uint32_t kMetaPad = 0xFFFFFFFFu;
+
+// Everything a kernel needs, passed by value (kernel arguments).
+struct Params {
+    // shapes
+    int S, T_max, H, I, E, El, lo, K, BM;
+    int chunks;           // routing chunks per shard
+    int max_blocks;       // pool capacity in BM blocks
+    uint32_t flags;
+    int tps[MEGA_MOE_MAX_SHARDS];
+    // workspace
+    uint32_t* status;     // [0] status bits, [1] number of pool blocks
+    int* chunk_hist;      // [S][chunks][E]
+    int* chunk_base;      // [S][chunks][El]
+    int* send;            // [S][E]
+    int* recv;            // [El][S]
+    int* recv_tot;        // [El]
+    int* pool_off;        // [El+1]
+    int* block_expert;    // [max_blocks]
+    int* block_index;     // [max_blocks]
+    int* table;           // [El][S][T_max]
+    uint8_t* pool_x;      // [rows][H]
+    float* pool_sf;       // [rows][H/128]
+    uint32_t* pool_meta;  // [rows][3]
+    uint8_t* l2_x;        // [rows][I]
+    float* l2_sf;         // [rows][I/128]
+    uint16_t* comb;       // [K][S*T_max][H]
+    float* gemm1_out;     // [rows][2I] or null
+    // caller tensors
+    const uint8_t* x;
+    const float* x_sf;
+    const int64_t* topk_idx;
+    const float* topk_w;
+    const uint8_t* w1;
+    const float* w1_sf;
+    const uint8_t* w2;
+    const float* w2_sf;
+    uint16_t* y;
+    int* cum;
+};
+
+// Launchers (one per translation unit), all on `stream`.  Return hipSuccess or the launch error.
+hipError_t launch_route(const Params& p, hipStream_t stream);
+hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream);
+hipError_t launch_gemm1(const Params& p, int num_cus, hipStream_t stream);
+hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
+hipError_t launch_combine(const Params& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = __lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+}  // namespace mm

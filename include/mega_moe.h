@@ -1,0 +1,179 @@
+/*
+ * mega_moe.h -- C ABI of the fused FP8 MoE layer for one GPU's expert-parallel share (MI355X, gfx950).
+ *
+ * The layer (pages: "Mega-MoE kernel code walkthrough: from Dispatch to WGMMA", sections 1, 4, 6 and 9;
+ * "MoE fused operators", DeepGEMM MegaMoE part) runs, on one HIP stream:
+ *   1. routing metadata: per-expert send counts and a [local_expert][source_shard][slot] index table
+ *      whose entries are t*K+k ("Mega-MoE notes, part 2: index table and pull", section 1);
+ *   2. a round-robin pull of the routed FP8 token rows and their scales into an expert-major pool whose
+ *      experts are padded to BLOCK_M rows (same page, 2.4-2.6);
+ *   3. FP8 grouped GEMM gate_up, per-128-K scale promotion (same page, 5.2);
+ *   4. SwiGLU and FP8 requantisation of the intermediate activation (walkthrough, section 6);
+ *   5. FP8 grouped GEMM down, cast to bf16 and scattered to a per-top-k combine buffer
+ *      ("DeepGEMM Mega MoE symmetric memory deep analysis", 8.1-8.2);
+ *   6. the top-k weighted combine back to token-major bf16 ("Dispatch/Combine: blog theory vs DeepEP vs
+ *      DeepGEMM Mega MoE", section 1; symmetric-memory page, 9.2).
+ * Source ranks are emulated as S token shards that all live in this GPU's HBM; this GPU owns global experts
+ * [local_rank*E_l, (local_rank+1)*E_l) (walkthrough, section 2).
+ *
+ * Conventions (all entry points):
+ *   - Every function returns 0 on success or a negative MEGA_MOE_ERR_* code; nothing throws.
+ *   - Pointers are device pointers unless the comment says host.  Device pointers must be 16-byte aligned.
+ *   - Tensors are dense, row-major (C order), with the shapes given below.  The library never frees or
+ *     keeps caller memory beyond the call, except the workspace, which a handle borrows until destroy.
+ *   - Work is enqueued on the given stream (hipStream_t passed as void*; NULL = the null stream) and is
+ *     asynchronous; inputs must stay alive and unmodified until the stream reaches the end of the call.
+ *   - Conditions only the device can see (an expert id >= E, a slot past T_max) do not fail the call:
+ *     the offending entry is skipped and a bit is latched in the workspace status word, which
+ *     mega_moe_status reads and clears.
+ */
+#ifndef MEGA_MOE_H
+#define MEGA_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEGA_MOE_MAX_SHARDS 64      /* S <= 64 */
+#define MEGA_MOE_MAX_TOPK 64        /* K <= 64 */
+#define MEGA_MOE_MAX_EXPERTS 4096   /* E <= 4096 */
+#define MEGA_MOE_MAX_LOCAL_EXPERTS 1024
+
+/* Return codes. */
+#define MEGA_MOE_OK 0
+#define MEGA_MOE_ERR_INVALID_ARG (-1)          /* null / misaligned pointer, negative size, bad stage mask */
+#define MEGA_MOE_ERR_UNSUPPORTED (-2)          /* a shape outside the supported set (see mega_moe_config) */
+#define MEGA_MOE_ERR_TOO_MANY_TOKENS (-3)      /* tokens_per_shard[s] > max_tokens_per_shard */
+#define MEGA_MOE_ERR_WORKSPACE_TOO_SMALL (-4)  /* workspace_bytes below mega_moe_workspace_bytes() */
+#define MEGA_MOE_ERR_HIP (-5)                  /* a HIP runtime call failed */
+
+/* Device status bits (latched in the workspace, read by mega_moe_status). */
+#define MEGA_MOE_STATUS_BAD_EXPERT_ID 0x1u     /* some topk_idx entry was >= E; that entry was skipped */
+#define MEGA_MOE_STATUS_SLOT_OVERFLOW 0x2u     /* some (expert, shard) needed more than T_max slots */
+#define MEGA_MOE_STATUS_BAD_LAYOUT 0x4u        /* a stage found workspace metadata no earlier stage wrote
+                                                  (only after mega_moe_forward_stages on hand-made data);
+                                                  the affected rows were skipped */
+
+/* Config flags. */
+#define MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT 0x1u   /* also store GEMM1's fp32 output [pool_rows, 2I] (tests) */
+
+/* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
+#define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, cumulative stats */
+#define MEGA_MOE_STAGE_FILL 0x2u      /* round-robin pull into the pool (needs ROUTE's outputs)       */
+#define MEGA_MOE_STAGE_GEMM1 0x4u     /* gate_up GEMM + SwiGLU + FP8 requant into the L2 pool          */
+#define MEGA_MOE_STAGE_GEMM2 0x8u     /* down GEMM, bf16, scatter to the combine buffer                */
+#define MEGA_MOE_STAGE_COMBINE 0x10u  /* top-k weighted combine into y                                 */
+#define MEGA_MOE_STAGE_ALL 0x1Fu
+#define MEGA_MOE_NUM_STAGES 5
+
+typedef struct mega_moe_config {
+    int32_t num_shards;           /* S: emulated source ranks, 1..64                                   */
+    int32_t max_tokens_per_shard; /* T_max: capacity per shard, >= 1                                    */
+    int32_t hidden;               /* H: multiple of 256, 256..16384                                     */
+    int32_t intermediate;         /* I: multiple of 128, 128..16384                                     */
+    int32_t num_experts;          /* E: global experts, 1..4096, a multiple of num_local_experts        */
+    int32_t num_local_experts;    /* E_l: experts owned by this GPU, 1..1024                            */
+    int32_t local_rank;           /* r: owns experts [r*E_l, (r+1)*E_l); 0 <= r < E/E_l                 */
+    int32_t topk;                 /* K: 1..64                                                           */
+    int32_t block_m;              /* BLOCK_M of the pool: 64 or 128; 0 picks from the expected rows     */
+    uint32_t flags;               /* MEGA_MOE_FLAG_*                                                    */
+} mega_moe_config;
+
+/* Byte offsets of the regions inside the workspace (for tests and tools) plus the resolved sizes. */
+typedef struct mega_moe_layout {
+    int32_t block_m;          /* resolved BLOCK_M                                                 */
+    int32_t route_chunks;     /* routing chunks per shard                                         */
+    int32_t max_pool_blocks;  /* capacity in BLOCK_M blocks: ceil(S*T_max*min(K,E_l)/BM) + E_l     */
+    int32_t reserved;
+    uint64_t status;          /* uint32 [0]: status bits; uint32 [1]: number of pool blocks (last forward) */
+    uint64_t chunk_hist;      /* int32 [S][chunks][E]                                             */
+    uint64_t chunk_base;      /* int32 [S][chunks][E_l]                                           */
+    uint64_t send;            /* int32 [S][E]: pairs of shard s routed to global expert e         */
+    uint64_t recv;            /* int32 [E_l][S]: recv[le][s] = send[s][r*E_l+le]                  */
+    uint64_t recv_tot;        /* int32 [E_l]                                                      */
+    uint64_t pool_off;        /* int32 [E_l+1]: first pool block of each local expert             */
+    uint64_t block_expert;    /* int32 [max_pool_blocks]: local expert of each pool block          */
+    uint64_t block_index;     /* int32 [max_pool_blocks]: m-block index inside its expert          */
+    uint64_t table;           /* int32 [E_l][S][T_max]: t*K+k, slots >= recv[le][s] unspecified    */
+    uint64_t pool_x;          /* uint8 [max_pool_blocks*BM][H] e4m3fn                              */
+    uint64_t pool_sf;         /* float [max_pool_blocks*BM][H/128]                                 */
+    uint64_t pool_meta;       /* uint32 [max_pool_blocks*BM][3] = {shard, token, k}; padding = ~0  */
+    uint64_t l2_x;            /* uint8 [max_pool_blocks*BM][I] e4m3fn                              */
+    uint64_t l2_sf;           /* float [max_pool_blocks*BM][I/128]                                 */
+    uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only        */
+    uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
+    uint64_t total;           /* bytes needed                                                     */
+} mega_moe_layout;
+
+typedef struct mega_moe_handle mega_moe_handle;
+
+/* Bytes of device workspace the config needs (host-only arithmetic; no GPU call).
+ * Errors: INVALID_ARG (null pointer), UNSUPPORTED (config outside the limits above). */
+int32_t mega_moe_workspace_bytes(const mega_moe_config* cfg, uint64_t* bytes_out /* host */);
+
+/* Create a handle over a caller-allocated workspace (the size query then caller allocation follows the
+ * pages' buffer setup: "DeepGEMM Mega MoE symmetric memory deep analysis", 5.1).  Zeroes the workspace on
+ * `stream`.  The workspace belongs to this handle until mega_moe_destroy; one handle must not run two
+ * forwards concurrently.  The current HIP device at init is the device the handle runs on.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP. */
+int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t workspace_bytes, void* stream,
+                      mega_moe_handle** out /* host */);
+
+/* The whole layer.  Shapes (S, T_max, H, I, E_l, K from the config):
+ *   tokens_per_shard  host int32 [S], each in 0..T_max: valid tokens of each shard (rows t >= T_s are
+ *                     neither read nor written)
+ *   x                 uint8 [S][T_max][H], e4m3fn codes
+ *   x_sf              float [S][T_max][H/128], per-token per-128-column scales
+ *   topk_idx          int64 [S][T_max][K], global expert ids; < 0 means "no expert"
+ *   topk_weights      float [S][T_max][K]
+ *   w1                uint8 [E_l][2I][H], e4m3fn; rows 0..I-1 gate, I..2I-1 up
+ *   w1_sf             float [E_l][2I/128][H/128], 128x128 block scales
+ *   w2                uint8 [E_l][H][I], e4m3fn
+ *   w2_sf             float [E_l][H/128][I/128]
+ *   y                 bf16 [S][T_max][H] output: y[s,t] = sum over k with a local expert of
+ *                     w[s,t,k] * Expert(x[s,t]); a token with no local expert gets a zero row
+ *   cum_recv_stats    int32 [E_l] or NULL: cum_recv_stats[le] += rows received by local expert le
+ *                     (the caller resets it; "DeepGEMM Mega MoE symmetric memory deep analysis", 10.1)
+ * Errors: INVALID_ARG, TOO_MANY_TOKENS, HIP.  Leaves the workspace ready for the next call. */
+int32_t mega_moe_forward(mega_moe_handle* h, const int32_t* tokens_per_shard, const void* x, const float* x_sf,
+                         const int64_t* topk_idx, const float* topk_weights, const void* w1, const float* w1_sf,
+                         const void* w2, const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream);
+
+/* As mega_moe_forward, running only the stages in `stages` (MEGA_MOE_STAGE_* bits).  A stage reads what
+ * the earlier stages left in the workspace, so tests can place their own intermediate data there
+ * (see mega_moe_query_layout) and run one stage on it.  Pointers a selected stage does not read may
+ * be NULL.  Errors: as mega_moe_forward; INVALID_ARG for stages == 0 or unknown bits. */
+int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32_t* tokens_per_shard,
+                                const void* x, const float* x_sf, const int64_t* topk_idx,
+                                const float* topk_weights, const void* w1, const float* w1_sf, const void* w2,
+                                const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream);
+
+/* Region offsets of the handle's workspace.  Errors: INVALID_ARG. */
+int32_t mega_moe_query_layout(const mega_moe_handle* h, mega_moe_layout* out /* host */);
+
+/* Synchronise `stream`, read and clear the device status word into *device_flags (host).
+ * Errors: INVALID_ARG, HIP. */
+int32_t mega_moe_status(mega_moe_handle* h, void* stream, uint32_t* device_flags /* host */);
+
+/* Per-stage timing.  mega_moe_set_timing(h, 1) starts (and resets) accumulation: every later forward
+ * records HIP events around each stage on its own stream, without synchronising.  mega_moe_stage_times
+ * waits for the recorded events and writes, per stage, the mean milliseconds over the forwards timed
+ * since the reset (MEGA_MOE_NUM_STAGES floats to ms; 0 for a stage that never ran) and the number of
+ * timed forwards to *count (host, may be NULL).  mega_moe_set_timing(h, 0) stops recording.
+ * Errors: INVALID_ARG, HIP. */
+int32_t mega_moe_set_timing(mega_moe_handle* h, int32_t enable);
+int32_t mega_moe_stage_times(mega_moe_handle* h, float* ms /* host, MEGA_MOE_NUM_STAGES */,
+                             int32_t* count /* host, nullable */);
+
+/* Release the handle (not the workspace).  Accepts NULL. */
+void mega_moe_destroy(mega_moe_handle* h);
+
+/* Static text for a return code. */
+const char* mega_moe_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEGA_MOE_H */

@@ -157,7 +157,7 @@ def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, to
     the table names at (le, source, slot) from the round-robin, plus metadata
     {rank, token, topk} ("Dispatch/Combine ... comparison", 6.2).  Rows past recv_tot in
     an expert's last block are padding: zero codes, zero scales, metadata all ones (the
-    pages skip those rows; their content is this build's choice).
+    pages skip those rows and leave their content open; zeros are the reading taken here).
     """
     El = rt.recv.shape[0]
     H = x.shape[2]
@@ -254,6 +254,14 @@ def expert_ffn_rows(a_codes, a_sf, w1_codes, w1_sf, w2_codes, w2_sf, intermediat
     return o
 
 
+def ffn_dequantised(a: np.ndarray, w1: np.ndarray, w2: np.ndarray, intermediate: int,
+                    gran: int = 128) -> np.ndarray:
+    """The same FFN steps as expert_ffn_rows on already dequantised rows and weights."""
+    h = swiglu(a @ w1.T, intermediate)
+    q, s = requant_rows(h, gran)
+    return bf16_round(dequant_rows_gran(q, s, gran) @ w2.T)
+
+
 def dequant_rows_gran(codes, sf, gran):
     v = e4m3fn_decode(codes)
     return v * np.repeat(np.asarray(sf, dtype=np.float64), gran, axis=-1)
@@ -314,7 +322,7 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
 
 
 def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
-                 local_rank: int, gran: int = 128) -> np.ndarray:
+                 local_rank: int, gran: int = 128, cache: Optional[dict] = None) -> np.ndarray:
     """y[s,t] evaluated on its own: no counts, no table, no pool.
 
     out(T) = sum over the token's local experts of w_k * Expert_k(T) ("Dispatch/Combine ...
@@ -332,7 +340,13 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
         if e < lo or e >= lo + num_local_experts:
             continue
         le = e - lo
-        o = expert_ffn_rows(a_codes, a_sf, inp["w1"][le], inp["w1_sf"][le], inp["w2"][le],
-                            inp["w2_sf"][le], I, gran)[0]
+        if cache is None:
+            o = expert_ffn_rows(a_codes, a_sf, inp["w1"][le], inp["w1_sf"][le], inp["w2"][le],
+                                inp["w2_sf"][le], I, gran)[0]
+        else:
+            if le not in cache:
+                cache[le] = (dequant_blocks(inp["w1"][le], inp["w1_sf"][le]),
+                             dequant_blocks(inp["w2"][le], inp["w2_sf"][le]))
+            o = ffn_dequantised(dequant_rows(a_codes, a_sf), cache[le][0], cache[le][1], I, gran)[0]
         acc += float(inp["topk_weights"][s, t, k]) * o
     return bf16_round(acc)

@@ -1,0 +1,129 @@
+"""The C-ABI library: it loads, exports every declared entry point, and its host-only checks work
+(no GPU: nothing here launches a kernel or allocates device memory)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dispatch_fp8_grouped_amd as mm
+from inputs import SHAPES
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mega_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mega_moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(mm.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mm.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+    lib = mm.lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_library_is_gfx950_code():
+    """The library (built here by build.py) carries a gfx950 code object and no other target."""
+    blob = open(mm.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+    for other in (b"--gfx942", b"--gfx90a", b"--gfx1100"):
+        assert other not in blob
+
+
+def cfg_of(name, **kw):
+    sh = SHAPES[name]
+    args = dict(num_shards=sh.num_shards, max_tokens_per_shard=sh.max_tokens_per_shard, hidden=sh.hidden,
+                intermediate=sh.intermediate, num_experts=sh.num_experts,
+                num_local_experts=sh.num_local_experts, topk=sh.topk, block_m=sh.block_m)
+    args.update(kw)
+    return mm.make_config(**args)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_workspace_bytes_matches_layout_formula(name):
+    sh = SHAPES[name]
+    n = mm.mega_moe_workspace_bytes(cfg_of(name))
+    S, T, H, I, El, K = (sh.num_shards, sh.max_tokens_per_shard, sh.hidden, sh.intermediate,
+                         sh.num_local_experts, sh.topk)
+    blocks = -(-(S * T * min(K, El)) // sh.block_m) + El
+    rows = blocks * sh.block_m
+    # the big regions alone: pool, l2 pool, combine buffer, table
+    floor = rows * H + rows * I + K * S * T * H * 2 + El * S * T * 4
+    assert floor <= n <= floor + rows * (H // 128 + I // 128 + 3) * 4 + 64 * 2 ** 20
+    assert n % 256 == 0
+    # the flag adds the fp32 GEMM1 output
+    n2 = mm.mega_moe_workspace_bytes(cfg_of(name, flags=mm.FLAG_KEEP_GEMM1_OUTPUT))
+    assert n2 >= n + rows * 2 * I * 4
+
+
+def test_block_m_auto_choice():
+    # decode: ~32 rows per expert -> 64; prefill: ~1024 -> 128
+    lib = mm.lib()
+    for name, want in [("decode", 64), ("prefill", 128), ("tiny", 64)]:
+        c = cfg_of(name, block_m=0)
+        a = mm.mega_moe_workspace_bytes(c)
+        b = mm.mega_moe_workspace_bytes(cfg_of(name, block_m=want))
+        assert a == b
+    assert lib is not None
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_shards", 0), ("num_shards", 65), ("hidden", 200), ("hidden", 384), ("intermediate", 100),
+    ("num_experts", 250), ("num_local_experts", 0), ("topk", 0), ("topk", 65), ("block_m", 96),
+    ("local_rank", 8), ("local_rank", -1), ("flags", 0x80), ("max_tokens_per_shard", 0),
+])
+def test_unsupported_configs_rejected(field, value):
+    c = cfg_of("prefill", **{field: value})
+    with pytest.raises(mm.MegaMoEError) as ei:
+        mm.mega_moe_workspace_bytes(c)
+    assert ei.value.code == mm.ERR_UNSUPPORTED
+
+
+def test_null_arguments_rejected_without_gpu():
+    lib = mm.lib()
+    c = cfg_of("tiny")
+    assert lib.mega_moe_workspace_bytes(None, None) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_workspace_bytes(ctypes.byref(c), None) == mm.ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    # null workspace, misaligned workspace, too-small workspace: all rejected before any HIP call
+    assert lib.mega_moe_init(ctypes.byref(c), None, 1 << 20, None, ctypes.byref(h)) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_init(ctypes.byref(c), 0x1008, 1 << 30, None, ctypes.byref(h)) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_init(ctypes.byref(c), 0x100000, 16, None, ctypes.byref(h)) == \
+        mm.ERR_WORKSPACE_TOO_SMALL
+    assert lib.mega_moe_init(None, 0x100000, 16, None, ctypes.byref(h)) == mm.ERR_INVALID_ARG
+    tps = (ctypes.c_int32 * 1)(64)
+    assert lib.mega_moe_forward(None, tps, *([None] * 11)) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_status(None, None, None) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_query_layout(None, None) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_set_timing(None, 1) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_stage_times(None, None, None) == mm.ERR_INVALID_ARG
+    lib.mega_moe_destroy(None)
+
+
+def test_strerror_texts():
+    for code in (mm.OK, mm.ERR_INVALID_ARG, mm.ERR_UNSUPPORTED, mm.ERR_TOO_MANY_TOKENS,
+                 mm.ERR_WORKSPACE_TOO_SMALL, mm.ERR_HIP):
+        assert mm.mega_moe_strerror(code) and mm.mega_moe_strerror(code) != "unknown error"
+    assert mm.mega_moe_strerror(-99) == "unknown error"
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "dispatch_fp8_grouped_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("the oracle", ""), f
+                assert "import inputs" not in text, f

@@ -1,0 +1,172 @@
+"""GPU edge cases: degenerate counts, empty and ragged inputs, sentinels, status bits, repeats,
+cumulative stats, host validation on a live handle, stage timing."""
+import numpy as np
+import pytest
+import torch
+
+import dispatch_fp8_grouped_amd as mm
+import oracle
+from inputs import SHAPES, MoEShape, make_inputs, to_numpy
+
+from gpu_util import Run, check_layout, tol_check, on_gpu, inputs_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _whole(run, inp):
+    sh = run.shape
+    ref = oracle.forward(inp, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m)
+    y = run.y_host()
+    valid = ~np.isnan(ref["y"])
+    tol_check(y[valid], ref["y"][valid], sh.name)
+    return ref
+
+
+def test_block_boundary_counts():
+    """Experts receiving 0, BM-1, BM, BM+1, 1 and 2*BM rows (BM = 64)."""
+    print("[case] block boundary counts", flush=True)
+    counts = [0, 63, 64, 65, 1, 128]
+    sh = MoEShape("bounds", 2, 161, 256, 256, 6, 6, 1, 64, seed=21)
+    inp = make_inputs(sh)
+    ids = np.concatenate([np.full(c, e) for e, c in enumerate(counts)])
+    np.random.default_rng(0).shuffle(ids)
+    flat = np.full(2 * 161, -1, dtype=np.int64)
+    flat[:len(ids)] = ids
+    inp["topk_idx"] = torch.from_numpy(flat.reshape(2, 161, 1))
+    run = Run(sh, inputs=inp)
+    n = inputs_np(run)
+    rt, off = check_layout(run, n)
+    assert rt.recv_tot.tolist() == counts
+    assert off.tolist() == [0, 0, 1, 2, 4, 5, 7]
+    _whole(run, n)
+    run.close()
+
+
+def test_all_tokens_one_expert_and_sentinels():
+    print("[case] one hot expert + -1 entries", flush=True)
+    sh = MoEShape("hot", 2, 300, 256, 128, 4, 4, 2, 64, seed=22)
+    inp = make_inputs(sh)
+    idx = torch.full((2, 300, 2), -1, dtype=torch.int64)
+    idx[:, :, 0] = 2
+    idx[0, ::7, 1] = 3
+    inp["topk_idx"] = idx
+    run = Run(sh, inputs=inp)
+    n = inputs_np(run)
+    rt, off = check_layout(run, n)
+    assert rt.recv_tot[2] == 600
+    _whole(run, n)
+    run.close()
+
+
+def test_random_negative_entries_and_remote_rank():
+    print("[case] sentinel entries, local_rank 3", flush=True)
+    sh = MoEShape("neg", 4, 96, 512, 256, 32, 8, 4, 64, local_rank=3, seed=23)
+    inp = make_inputs(sh)
+    drop = torch.rand(inp["topk_idx"].shape, generator=torch.Generator().manual_seed(1)) < 0.2
+    inp["topk_idx"][drop] = -1
+    run = Run(sh, inputs=inp, tokens_per_shard=None)
+    n = inputs_np(run)
+    check_layout(run, n)
+    _whole(run, n)
+    run.close()
+
+
+def test_repeat_calls_identical_and_state_clean():
+    """Two calls give identical bits; a call on other routing in between does not leak state."""
+    print("[case] repeat calls", flush=True)
+    sh = SHAPES["mid"].replace(max_tokens_per_shard=256)
+    a = make_inputs(sh, device="cuda")
+    b = make_inputs(sh, device="cuda", seed=99, tokens_per_shard=[256, 3, 100, 0])
+    moe = mm.MegaMoE.from_shape(sh)
+    y1 = moe(a)
+    moe(b)
+    y2 = moe(a)
+    moe(a)
+    y3 = moe(a)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    assert moe.status() == 0
+    moe.close()
+
+
+def test_cumulative_recv_stats():
+    print("[case] cumulative stats", flush=True)
+    sh = SHAPES["tiny"]
+    cum = torch.full((sh.num_local_experts,), 5, dtype=torch.int32, device="cuda")
+    run = Run(sh, cum=cum, repeat=3)
+    n = inputs_np(run)
+    rt = oracle.route(n["topk_idx"], n["tokens_per_shard"], sh.num_experts, sh.num_local_experts, 0)
+    assert cum.cpu().numpy().tolist() == (5 + 3 * rt.recv_tot).tolist()
+    run.close()
+
+
+def test_bad_expert_id_sets_status_and_is_skipped():
+    print("[case] bad expert id", flush=True)
+    sh = SHAPES["tiny"]
+    inp = make_inputs(sh)
+    inp["topk_idx"][0, 5, 1] = 8        # E = 8
+    inp["topk_idx"][0, 9, 0] = 1000
+    run = Run(sh, inputs=inp)
+    assert run.status & mm.STATUS_BAD_EXPERT_ID
+    assert run.moe.status() == 0        # read-and-clear
+    n = inputs_np(run)
+    check_layout(run, n)
+    _whole(run, n)
+    run.close()
+
+
+def test_slot_overflow_status_and_clamped_layout():
+    print("[case] slot overflow", flush=True)
+    sh = MoEShape("dup", 1, 4, 256, 128, 2, 2, 2, 64, seed=24)
+    inp = make_inputs(sh)
+    inp["topk_idx"][:] = 0               # the same expert twice per token: 8 entries, 4 slots
+    run = Run(sh, inputs=inp)
+    assert run.status & mm.STATUS_SLOT_OVERFLOW
+    n = inputs_np(run)
+    rt, _ = check_layout(run, n)
+    assert rt.recv[0, 0] == 4
+    run.close()
+
+
+def test_host_validation_on_live_handle():
+    sh = SHAPES["tiny"]
+    inp = on_gpu(make_inputs(sh))
+    moe = mm.MegaMoE.from_shape(sh)
+    with pytest.raises(mm.MegaMoEError) as ei:
+        moe.forward([65], inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_weights"], inp["w1"],
+                    inp["w1_sf"], inp["w2"], inp["w2_sf"])
+    assert ei.value.code == mm.ERR_TOO_MANY_TOKENS
+    with pytest.raises(mm.MegaMoEError) as ei:
+        mm.mega_moe_forward_stages(moe.h, 0x20, [64], inp["x"], inp["x_sf"], inp["topk_idx"],
+                                   inp["topk_weights"], inp["w1"], inp["w1_sf"], inp["w2"], inp["w2_sf"],
+                                   torch.empty(1, 64, 256, dtype=torch.bfloat16, device="cuda"))
+    assert ei.value.code == mm.ERR_INVALID_ARG
+    with pytest.raises(mm.MegaMoEError) as ei:     # GEMM1 without weights
+        mm.mega_moe_forward_stages(moe.h, mm.STAGE_GEMM1, [64], None, None, None, None, None, None, None,
+                                   None, None)
+    assert ei.value.code == mm.ERR_INVALID_ARG
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mm.MegaMoEError) as ei:
+        mm.mega_moe_init(moe.cfg, small)
+    assert ei.value.code == mm.ERR_WORKSPACE_TOO_SMALL
+    moe.close()
+
+
+def test_stage_timing():
+    sh = SHAPES["tiny"]
+    inp = on_gpu(make_inputs(sh))
+    moe = mm.MegaMoE.from_shape(sh)
+    mm.mega_moe_set_timing(moe.h, True)
+    for _ in range(70):                 # more forwards than the event ring holds
+        moe(inp)
+    t, n = mm.mega_moe_stage_times(moe.h, with_count=True)
+    assert n == 70 and len(t) == 5 and all(v > 0 for v in t)
+    mm.mega_moe_set_timing(moe.h, True)  # reset
+    moe(inp, stages=mm.STAGE_ROUTE | mm.STAGE_FILL)
+    t, n = mm.mega_moe_stage_times(moe.h, with_count=True)
+    assert n == 1 and t[0] > 0 and t[1] > 0 and t[2] == t[3] == t[4] == 0
+    mm.mega_moe_set_timing(moe.h, False)
+    moe(inp)
+    assert mm.mega_moe_stage_times(moe.h, with_count=True)[1] == 0     # the reset cleared the count
+    moe.close()
