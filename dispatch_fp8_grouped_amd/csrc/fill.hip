@@ -16,6 +16,8 @@
 namespace mm {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
 constexpr int kFillThreads = 256;
 constexpr int kUnroll = 8;   // 8 x 64 lanes x 16 B = 8 KB per batch (H <= 8192 in one batch)
 
@@ -37,11 +39,11 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
         const int le = min(max(p.block_expert[b], 0), p.El - 1);
         const int j = p.block_index[b] * p.BM + (int)(row - (long)b * p.BM);
         const int n = p.recv_tot[le];
-        uint4* dst = reinterpret_cast<uint4*>(p.pool_x + (size_t)row * p.H);
+        v4i* dst = reinterpret_cast<v4i*>(p.pool_x + (size_t)row * p.H);
         float* dsf = p.pool_sf + (size_t)row * SF;
         uint32_t* meta = p.pool_meta + (size_t)row * 3;
         if (j >= n) {
-            const uint4 z = make_uint4(0, 0, 0, 0);
+            const v4i z = {0, 0, 0, 0};
             for (int i = lane; i < H16; i += 64) dst[i] = z;
             for (int i = lane; i < SF; i += 64) dsf[i] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
@@ -72,16 +74,16 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
         const int v = slot < p.T_max ? p.table[((size_t)le * p.S + src) * p.T_max + slot] : -1;
         if (v < 0 || v >= p.tps[src] * p.K) {              // never for metadata the routing stage made
             if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
-            for (int i = lane; i < H16; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
+            for (int i = lane; i < H16; i += 64) dst[i] = v4i{0, 0, 0, 0};
             for (int i = lane; i < SF; i += 64) dsf[i] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
             continue;
         }
         const int t = v / p.K, k = v - t * p.K;
         const size_t srow = (size_t)src * p.T_max + t;
-        const uint4* sp = reinterpret_cast<const uint4*>(p.x + srow * p.H);
+        const v4i* sp = reinterpret_cast<const v4i*>(p.x + srow * p.H);
         for (int base = 0; base < H16; base += 64 * kUnroll) {
-            uint4 r[kUnroll];
+            v4i r[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int i = base + u * 64 + lane;

@@ -12,24 +12,35 @@
 // MFMA into a fresh accumulator P, then final += (sa[m, kb] * sw[n_block, kb]) * P in fp32.
 //
 // Tiling: one work-group of 8 waves computes a BM x 256 tile (BM tokens = one pool block, 256 weight
-// rows), K step 128, A and B staged through a double-buffered LDS (global -> registers -> LDS, XOR
-// swizzle of 16-byte chunks).  The MFMA's A operand is the weight tile and its B operand the token tile,
-// so each lane's four outputs share one token and one weight block: the promotion needs one scale per
+// rows) in K steps of 128.  The MFMA's A operand is the weight tile and its B operand the token tile, so
+// each lane's four outputs share one token and one weight block and the promotion needs one scale per
 // token subtile.  Wave (wm, wn) owns tokens [wm*BM/2, +BM/2) and 64 weight rows:
 //   GEMM1: gate rows nt*128 + wn*32 + [0,32) and the matching up rows I + nt*128 + wn*32 + [0,32),
 //          so gate and up of one output column sit in the same lane;
 //   GEMM2: hidden rows nt*256 + wn*64 + [0,64).
-// The kernel is persistent: one work-group per CU walks the (block, n-tile) space; consecutive
-// work-groups of one XCD take neighbouring tiles (8 pool blocks x 4 n-tiles share A and B in L2).
+//
+// Pipeline: a K step's operands (A and B tiles, the token scales, the two weight-block scales and, for
+// GEMM2, the tile's pool metadata) arrive by LDS DMA (global_load_lds) into one of three LDS stages.
+// The persistent work-group walks its (tile, K step) sequence as one stream: step s waits until stage s
+// has landed (vmcnt counts only the one younger stage), barriers, issues the DMA of step s+2 into the
+// stage freed by step s-1, then runs its MFMAs; the next tile's first steps load during the current
+// tile's last ones.  Every step issues the same number of DMA instructions (past the end the last step
+// is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
+// XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
+// Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of a group of eight
+// pool blocks, which share A and B through that XCD's L2.
 #include "mm_internal.h"
 
 namespace mm {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kThreads = 512;
+constexpr int kStages = 3;
 constexpr int kGroupBlocks = 8;   // pool blocks per tile group
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -45,12 +56,9 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7
 __device__ __forceinline__ v8i load_frag(const uint8_t* lds, int row0, int lane) {
     const int r = row0 + (lane & 15);
     const int g = lane >> 4;
-    const uint4 lo = *reinterpret_cast<const uint4*>(lds + swz(r, 2 * g));
-    const uint4 hi = *reinterpret_cast<const uint4*>(lds + swz(r, 2 * g + 1));
-    v8i f;
-    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-    return f;
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + swz(r, 2 * g));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + swz(r, 2 * g + 1));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Four fp32 -> four e4m3fn codes (round to nearest even, saturating), byte i from value i.  The
@@ -63,151 +71,198 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(float a, float b, float c, float d
     return (uint32_t)v;
 }
 
+// DMA of 16 (or 4) bytes per active lane from `src` to LDS at `dst` + lane * size; dst is wave-uniform.
+// Written as inline asm: the waits for these writes are placed by hand (wait_stage_barrier), and the
+// compiler, which cannot tell the three stages apart, would otherwise drain every DMA before each LDS read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_ptr)const_cast<void*>(p);
+}
+__device__ __forceinline__ void dma16(const void* src, const void* dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, const void* dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding, then barrier.  The
+// compiler's __syncthreads would drain every LDS DMA in flight; this keeps the younger stage loading.
+template <int N>
+__device__ __forceinline__ void wait_stage_barrier() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int BM, bool kGemm1>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
     constexpr int TM = BM / 32;                 // 16-token subtiles per wave
     constexpr int WN = 4;                       // 16-row weight subtiles per wave
-    constexpr int A_CH = BM * 8 / kThreads;     // 16-byte A chunks per thread per K step
-    constexpr int B_CH = 256 * 8 / kThreads;    // 16-byte B chunks per thread per K step
-    static_assert(A_CH >= 1 && B_CH == 4, "tile shape");
+    constexpr int A_INS = BM / 64;              // 1 KB A DMA instructions per wave and step
+    constexpr int B_INS = 4;                    // 1 KB B DMA instructions per wave and step
+    constexpr int SA_LANES = BM / 8;            // token scales per wave and step
+    constexpr int META_LANES = BM * 3 / 8;      // metadata dwords per wave and step (GEMM2)
+    constexpr int DMA_PER_STEP = A_INS + B_INS + 2 + (kGemm1 ? 0 : 1);
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][256 * 128];
-    __shared__ float sSA[2][BM];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * 128];
+    __shared__ __attribute__((aligned(16))) float sSA[kStages][BM];
+    __shared__ __attribute__((aligned(16))) float sSW[kStages][8][4];
+    __shared__ __attribute__((aligned(16))) uint32_t sMeta[kStages][kGemm1 ? 4 : BM * 3];
     __shared__ float sRed[BM][4];
+    __shared__ int sOff[MEGA_MOE_MAX_LOCAL_EXPERTS + 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int rr = lane & 15, g = lane >> 4;
     const int Kdim = kGemm1 ? p.H : p.I;
     const int KB = Kdim >> 7;
     const int NT = kGemm1 ? (p.I >> 7) : (p.H >> 8);
     const int nblocks = min((int)p.status[1], p.max_blocks);
-    const long ngroups = (nblocks + kGroupBlocks - 1) / kGroupBlocks;
-    const long ntiles = ngroups * kGroupBlocks * NT;
+    const int ntiles = nblocks * NT;
     const int G = gridDim.x;                    // a multiple of 8
     const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (logical >= ntiles) return;
+    const int my_tiles = (ntiles - 1 - logical) / G + 1;
+    const int nsteps = my_tiles * KB;
+    const int full = (nblocks / kGroupBlocks) * kGroupBlocks * NT;
+    const int tail = nblocks % kGroupBlocks;
 
-    for (long tile = logical; tile < ntiles; tile += G) {
-        const long grp = tile / (kGroupBlocks * NT);
-        const int rem = (int)(tile - grp * (kGroupBlocks * NT));
-        const int nt = rem / kGroupBlocks;
-        const int b = (int)(grp * kGroupBlocks) + (rem - nt * kGroupBlocks);
-        if (b >= nblocks) continue;
-        const int le = p.block_expert[b];
-        if (le < 0 || le >= p.El) continue;
-        const size_t row0 = (size_t)b * BM;
-        const uint8_t* A = (kGemm1 ? p.pool_x : p.l2_x) + row0 * Kdim;
-        const float* Asf = (kGemm1 ? p.pool_sf : p.l2_sf) + row0 * KB;
-        const uint8_t* W = kGemm1 ? p.w1 + (size_t)le * (2 * p.I) * p.H : p.w2 + (size_t)le * p.H * p.I;
+    // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
+    // waits on a global load of its own
+    for (int i = tid; i <= p.El; i += kThreads) sOff[i] = p.pool_off[i];
+    __syncthreads();
+
+    // tile j of this work-group -> pool block, n tile and local expert (no holes: the last group of
+    // blocks may be short)
+    auto tile_of = [&](int j, int& b, int& nt, int& le) {
+        const int t = logical + j * G;
+        if (t < full) {
+            const int grp = t / (kGroupBlocks * NT);
+            const int rem = t - grp * (kGroupBlocks * NT);
+            nt = rem / kGroupBlocks;
+            b = grp * kGroupBlocks + (rem - nt * kGroupBlocks);
+        } else {
+            const int rem = t - full;
+            nt = rem / tail;
+            b = full / NT + (rem - nt * tail);
+        }
+        int lo = 0, hi = p.El;              // last expert whose first block is <= b
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sOff[mid] <= b) lo = mid; else hi = mid;
+        }
+        le = lo;
+    };
+
+    // per-lane parts of the DMA addresses (the same for every tile and step)
+    int a_off[A_INS], b_off[B_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+        const int r = (i * 8 + wave) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        a_off[i] = r * Kdim + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int r = (i * 8 + wave) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        const int wr = kGemm1 ? (r < 128 ? r : p.I - 128 + r) : r;     // + the tile's row base
+        b_off[i] = wr * Kdim + c * 16;
+    }
+    const int sa_off = (wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * KB;
+
+    // issue side: the step whose DMA goes out next, walked incrementally (tile ij, K step ikb)
+    int ij = 0, ikb = 0, ibuf = 0, ib = 0, int_ = 0, ile = 0;
+    tile_of(0, ib, int_, ile);
+    auto issue = [&]() {
+        const size_t row0 = (size_t)ib * BM;
+        const int kb = ikb, buf = ibuf, nt = int_, le = ile;
+        const uint8_t* A = (kGemm1 ? p.pool_x : p.l2_x) + row0 * Kdim + kb * 128;
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i) dma16(A + a_off[i], &sA[buf][(i * 8 + wave) * 1024]);
+        const uint8_t* W = kGemm1 ? p.w1 + ((size_t)le * (2 * p.I) + nt * 128) * p.H
+                                  : p.w2 + ((size_t)le * p.H + nt * 256) * p.I;
+        W += kb * 128;
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i) dma16(W + b_off[i], &sB[buf][(i * 8 + wave) * 1024]);
+        const float* Asf = (kGemm1 ? p.pool_sf : p.l2_sf) + row0 * KB + kb;
+        if (lane < SA_LANES) dma4(Asf + sa_off, &sSA[buf][wave * SA_LANES]);
         const float* Wsf = kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
                                   : p.w2_sf + (size_t)le * (p.H >> 7) * KB;
+        int blk;
+        if (kGemm1) blk = lane == 0 ? nt : (p.I >> 7) + nt;          // gate block, up block
+        else blk = nt * 2 + (wn >> 1);
+        if (lane < 2) dma4(Wsf + (size_t)blk * KB + kb, &sSW[buf][wave][0]);
+        if (!kGemm1) {
+            if (lane < META_LANES)
+                dma4(p.pool_meta + row0 * 3 + wave * META_LANES + lane, &sMeta[buf][wave * META_LANES]);
+        }
+        // advance; past the last step the last step is loaded again (constant DMA count per step)
+        ibuf = ibuf == kStages - 1 ? 0 : ibuf + 1;
+        if (ikb + 1 < KB) {
+            ++ikb;
+        } else if (ij + 1 < my_tiles) {
+            ikb = 0;
+            ++ij;
+            tile_of(ij, ib, int_, ile);
+        }
+    };
 
-        // global source / LDS destination of this thread's chunks
-        const uint8_t* a_src[A_CH];
-        int a_dst[A_CH];
+    // LDS row of this wave's weight subtile a
+    int wrow0[WN];
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int ci = tid + i * kThreads, r = ci >> 3, c = ci & 7;
-            a_src[i] = A + (size_t)r * Kdim + c * 16;
-            a_dst[i] = swz(r, c);
-        }
-        const uint8_t* b_src[B_CH];
-        int b_dst[B_CH];
+    for (int a = 0; a < WN; ++a) {
+        if (kGemm1) wrow0[a] = (a < 2 ? 0 : 128) + wn * 32 + (a & 1) * 16;
+        else wrow0[a] = wn * 64 + a * 16;
+    }
+
+    v4f acc[WN][TM];
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int ci = tid + i * kThreads, r = ci >> 3, c = ci & 7;
-            int wrow;
-            if (kGemm1) wrow = r < 128 ? nt * 128 + r : p.I + nt * 128 + (r - 128);
-            else wrow = nt * 256 + r;
-            b_src[i] = W + (size_t)wrow * Kdim + c * 16;
-            b_dst[i] = swz(r, c);
+    for (int a = 0; a < WN; ++a)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    issue();
+    issue();
+    int cj = 0, ckb = 0, cbuf = 0;      // compute side: tile, K step, stage
+    for (int s = 0; s < nsteps; ++s) {
+        wait_stage_barrier<DMA_PER_STEP>();     // stage s landed in every wave; stage s-1 is free
+        issue();
+        const int buf = cbuf, kb = ckb, j = cj;
+        cbuf = cbuf == kStages - 1 ? 0 : cbuf + 1;
+        if (++ckb == KB) { ckb = 0; ++cj; }
+
+        const float sw0 = sSW[buf][wave][0], sw1 = sSW[buf][wave][1];
+        float sa[TM];
+        v8i xf[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int r0 = wm * (BM / 2) + t * 16;
+            sa[t] = sSA[buf][r0 + rr];
+            xf[t] = load_frag(sA[buf], r0, lane);
         }
-        // LDS row of this wave's weight subtile a
-        int wrow0[WN];
 #pragma unroll
         for (int a = 0; a < WN; ++a) {
-            if (kGemm1) wrow0[a] = (a < 2 ? 0 : 128) + wn * 32 + (a & 1) * 16;
-            else wrow0[a] = wn * 64 + a * 16;
-        }
-        // scale rows of the weight blocks this wave touches
-        const float* swp0;
-        const float* swp1;
-        if (kGemm1) {
-            swp0 = Wsf + (size_t)nt * KB;                          // gate block
-            swp1 = Wsf + (size_t)((p.I >> 7) + nt) * KB;           // up block
-        } else {
-            swp0 = Wsf + (size_t)(nt * 2 + (wn >> 1)) * KB;
-            swp1 = swp0;
-        }
-
-        v4f acc[WN][TM];
-#pragma unroll
-        for (int a = 0; a < WN; ++a)
-#pragma unroll
-            for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-        uint4 ra[A_CH], rb[B_CH];
-        float rsa = 0.f;
-        // prologue: K step 0 into buffer 0
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i]);
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i]);
-        if (tid < BM) rsa = Asf[(size_t)tid * KB];
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(&sA[0][a_dst[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(&sB[0][b_dst[i]]) = rb[i];
-        if (tid < BM) sSA[0][tid] = rsa;
-        __syncthreads();
-
-        for (int kb = 0; kb < KB; ++kb) {
-            const int cur = kb & 1;
-            const bool more = kb + 1 < KB;
-            if (more) {
-                const int off = (kb + 1) * 128;
-#pragma unroll
-                for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
-#pragma unroll
-                for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + off);
-                if (tid < BM) rsa = Asf[(size_t)tid * KB + kb + 1];
-            }
-            const float sw0 = swp0[kb], sw1 = swp1[kb];
-            float sa[TM];
-            v8i xf[TM];
+            const v8i wf = load_frag(sB[buf], wrow0[a], lane);
+            const float swa = (kGemm1 && a >= 2) ? sw1 : sw0;
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                const int r0 = wm * (BM / 2) + t * 16;
-                sa[t] = sSA[cur][r0 + rr];
-                xf[t] = load_frag(sA[cur], r0, lane);
+                const v4f pr = mfma_fp8(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
+                acc[a][t] += (sa[t] * swa) * pr;
             }
-#pragma unroll
-            for (int a = 0; a < WN; ++a) {
-                const v8i wf = load_frag(sB[cur], wrow0[a], lane);
-                const float swa = (kGemm1 && a >= 2) ? sw1 : sw0;
-#pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    const v4f pr = mfma_fp8(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
-                    const float sc = sa[t] * swa;
-                    acc[a][t] += sc * pr;
-                }
-            }
-            if (more) {
-#pragma unroll
-                for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(&sA[cur ^ 1][a_dst[i]]) = ra[i];
-#pragma unroll
-                for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(&sB[cur ^ 1][b_dst[i]]) = rb[i];
-                if (tid < BM) sSA[cur ^ 1][tid] = rsa;
-            }
-            __syncthreads();
         }
+        if (kb != KB - 1) continue;
 
-        // ------------------------------------------------------------------ epilogues
+        // ------------------------------------------------------------------ epilogue of tile j
         // lane holds acc[a][t][i]: weight row wrow0[a] + 4g + i, token wm*BM/2 + 16t + rr
+        int b, nt, le_unused;
+        tile_of(j, b, nt, le_unused);
+        (void)le_unused;
+        const size_t row0 = (size_t)b * BM;
         if (kGemm1) {
             float h[2][TM][4];
-            float amax[TM];
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 float m = 0.f;
@@ -222,43 +277,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
                     }
                 m = fmaxf(m, __shfl_xor(m, 16));
                 m = fmaxf(m, __shfl_xor(m, 32));
-                amax[t] = m;
                 if (g == 0) sRed[wm * (BM / 2) + t * 16 + rr][wn] = m;
             }
-            __syncthreads();
+            lds_barrier();
             const int I = p.I;
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 const int tok = wm * (BM / 2) + t * 16 + rr;
                 const float* red = sRed[tok];
                 const float am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-                const float s = fmaxf(am, 1e-4f) / 448.0f;
+                const float sc = fmaxf(am, 1e-4f) / 448.0f;
                 const size_t row = row0 + tok;
 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
                     const int col = nt * 128 + wn * 32 + a * 16 + 4 * g;
-                    const uint32_t q = cvt_fp8x4(h[a][t][0] / s, h[a][t][1] / s, h[a][t][2] / s,
-                                                 h[a][t][3] / s);
+                    const uint32_t q = cvt_fp8x4(h[a][t][0] / sc, h[a][t][1] / sc, h[a][t][2] / sc,
+                                                 h[a][t][3] / sc);
                     *reinterpret_cast<uint32_t*>(p.l2_x + row * I + col) = q;
                     if (p.gemm1_out) {
                         float* go = p.gemm1_out + row * (size_t)(2 * I);
-                        *reinterpret_cast<float4*>(go + col) =
-                            make_float4(acc[a][t][0], acc[a][t][1], acc[a][t][2], acc[a][t][3]);
-                        *reinterpret_cast<float4*>(go + I + col) =
-                            make_float4(acc[a + 2][t][0], acc[a + 2][t][1], acc[a + 2][t][2], acc[a + 2][t][3]);
+                        *reinterpret_cast<v4f*>(go + col) = acc[a][t];
+                        *reinterpret_cast<v4f*>(go + I + col) = acc[a + 2][t];
                     }
                 }
-                if (wn == 0 && g == 0) p.l2_sf[row * (size_t)(I >> 7) + nt] = s;
+                if (wn == 0 && g == 0) p.l2_sf[row * (size_t)(I >> 7) + nt] = sc;
             }
-            (void)amax;
-            __syncthreads();   // sRed is rewritten by the next tile
+            lds_barrier();      // sRed is rewritten by the next tile
         } else {
             const size_t plane = (size_t)p.S * p.T_max;
+            const uint32_t* meta = sMeta[buf];
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 const int tok = wm * (BM / 2) + t * 16 + rr;
-                const uint32_t* meta = p.pool_meta + (row0 + tok) * 3;
-                const uint32_t ms = meta[0], mt = meta[1], mk = meta[2];
+                const uint32_t ms = meta[tok * 3], mt = meta[tok * 3 + 1], mk = meta[tok * 3 + 2];
                 if (ms >= (uint32_t)p.S || mt >= (uint32_t)p.T_max || mk >= (uint32_t)p.K) continue;  // padding
                 uint16_t* dst = p.comb + ((size_t)mk * plane + (size_t)ms * p.T_max + mt) * p.H;
 #pragma unroll
@@ -271,7 +322,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
                 }
             }
         }
+#pragma unroll
+        for (int a = 0; a < WN; ++a)
+#pragma unroll
+            for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
     }
+    wait_all_vm();      // no LDS DMA may still be landing when the work-group ends
 }
 
 template <int BM, bool kGemm1>
