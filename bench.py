@@ -51,6 +51,20 @@ def algorithmic(shape, R, N):
     )
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE record, or None
+    when that record was taken on other GEMM source than the one built here (or another workload)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm1_prefill_traffic.json")
+    if workload != "prefill" or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "dispatch_fp8_grouped_amd", "csrc", "gemm.hip"), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec.get("gemm_source_sha256"):
+        return None
+    return rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
+
+
 def cpu_baseline(shape, inp_gpu, n_experts: int):
     """The CPU oracle, as is, on a bounded sample of the same workload: the whole routing and pool
     fill, then the FFN of the first n_experts local experts.  Rate = their routed rows / seconds."""
@@ -78,8 +92,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=4)
+    ap.add_argument("--cpu-experts", type=int, default=8)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="instead of the layer, run a plain elementwise copy of this many MiB five times "
+                         "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy * 2 ** 20 // 4
+        src = torch.randint(0, 2 ** 30, (n,), dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5,
+                          "kernel": "torch.bitwise_not (elementwise int32)"}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's expert-parallel share; --gpus {args.gpus} is not supported "
               f"(source ranks are emulated as shards on the one GPU)", file=sys.stderr)
@@ -149,7 +177,9 @@ def main():
         "gemm_tflops": gemm_tflops,
         "roofline": {"bound": "mfma", "kernel": "gemm1 (gate_up + SwiGLU + requant)",
                      "achieved": g1_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": g1_tflops / FP8_PEAK_TFLOPS, "traffic": None},
+                     "frac": g1_tflops / FP8_PEAK_TFLOPS, "traffic": measured_traffic(args.workload),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic": "4*R*H*I flop per launch, R = routed rows"},
         "stages_ms": st,
         "stages": {
             "route": {"GB/s": gbs(w["route_bytes"], st["route"])},

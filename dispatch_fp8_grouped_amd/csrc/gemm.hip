@@ -29,6 +29,8 @@
 // XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
 // Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of a group of eight
 // pool blocks, which share A and B through that XCD's L2.
+#include <type_traits>
+
 #include "mm_internal.h"
 
 namespace mm {
@@ -39,7 +41,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int kThreads = 512;
+constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
 constexpr int kStages = 3;
 constexpr int kGroupBlocks = 8;   // pool blocks per tile group
 
@@ -48,8 +50,11 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// 16-byte chunk c of a 128-byte LDS row r sits at position c ^ (r & 7).
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// 16-byte chunk c of a 128-byte LDS row r sits at position c ^ (r & 7) ^ ((r >> 3) & 1): the 16 rows
+// of one fragment read land in 16 different 16-byte bank slots whether the LDS serves 8 or 16 lanes of a
+// 128-bit read per cycle.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + (swz_chunk(r, c) << 4); }
 
 // Fragment of 16 rows x 128 K bytes for one MFMA operand: lane l takes row (l & 15) and the 32 bytes
 // [32*(l>>4), +32).  A and B use the same lane -> K mapping, so the product sums every K exactly once.
@@ -71,52 +76,71 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(float a, float b, float c, float d
     return (uint32_t)v;
 }
 
-// DMA of 16 (or 4) bytes per active lane from `src` to LDS at `dst` + lane * size; dst is wave-uniform.
-// Written as inline asm: the waits for these writes are placed by hand (wait_stage_barrier), and the
-// compiler, which cannot tell the three stages apart, would otherwise drain every DMA before each LDS read.
+// LDS DMA: every active lane copies 16 (or 4) bytes from base + off to LDS at dst + lane * size (dst and
+// base wave-uniform, off per lane).  Inline asm: the waits for these writes are placed by hand
+// (wait_stage_barrier); the compiler, which cannot tell the three stages apart, would otherwise drain
+// every DMA in flight before each LDS read.  M0 is set in the same statement.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(lds_ptr)const_cast<void*>(p);
 }
-__device__ __forceinline__ void dma16(const void* src, const void* dst) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+// A wave-uniform pointer placed in scalar registers (the DMA takes its base there).
+__device__ __forceinline__ const void* sgpr_ptr(const void* ptr) {
+    const uint64_t v = (uint64_t)(uintptr_t)ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ void dma4(const void* src, const void* dst) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, const void* dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, const void* dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding, then barrier.  The
 // compiler's __syncthreads would drain every LDS DMA in flight; this keeps the younger stage loading.
 template <int N>
-__device__ __forceinline__ void wait_stage_barrier() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int BM, bool kGemm1>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
-    constexpr int TM = BM / 32;                 // 16-token subtiles per wave
-    constexpr int WN = 4;                       // 16-row weight subtiles per wave
-    constexpr int A_INS = BM / 64;              // 1 KB A DMA instructions per wave and step
-    constexpr int B_INS = 4;                    // 1 KB B DMA instructions per wave and step
-    constexpr int SA_LANES = BM / 8;            // token scales per wave and step
-    constexpr int META_LANES = BM * 3 / 8;      // metadata dwords per wave and step (GEMM2)
-    constexpr int DMA_PER_STEP = A_INS + B_INS + 2 + (kGemm1 ? 0 : 1);
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.
+template <int BM, int NW, bool kGemm1>
+__global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
+    constexpr int NWN = NW / 2;                 // compute waves along the weight (N) side
+    constexpr int TM = BM / 32;                 // 16-token subtiles per wave (wave covers BM/2 tokens)
+    constexpr int WROWS = 256 / NWN;            // weight rows per wave
+    constexpr int WN = WROWS / 16;              // 16-row weight subtiles per wave
+    constexpr int HC = WROWS / 2;               // GEMM1: output columns per wave (gate + up halves)
+    constexpr int NMF = TM * WN;                // MFMAs per wave and K step
+    constexpr int A_INS = BM / (8 * NW);        // 1 KB A DMA instructions per wave and step
+    constexpr int B_INS = 32 / NW;              // 1 KB B DMA instructions per wave and step
+    constexpr int SA_LANES = BM / NW;           // token scales per wave and step
+    constexpr int META_PER_WAVE = BM * 3 / NW;  // metadata dwords per wave and step (GEMM2)
+    constexpr int META_INS = (META_PER_WAVE + 63) / 64;
+    constexpr int DMA_PER_STEP = A_INS + B_INS + 2 + (kGemm1 ? 0 : META_INS);
+    static_assert(A_INS >= 1 && B_INS >= 1 && SA_LANES <= 64, "tile shape");
+    static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * 128];
     __shared__ __attribute__((aligned(16))) float sSA[kStages][BM];
-    __shared__ __attribute__((aligned(16))) float sSW[kStages][8][4];
-    __shared__ __attribute__((aligned(16))) uint32_t sMeta[kStages][kGemm1 ? 4 : BM * 3];
-    __shared__ float sRed[BM][4];
+    __shared__ __attribute__((aligned(16))) float sSW[kStages][NW][4];
+    __shared__ __attribute__((aligned(16))) uint32_t sMeta[kStages][kGemm1 ? 4 : META_INS * 64 * NW];
+    __shared__ float sRed[BM][NWN];
     __shared__ int sOff[MEGA_MOE_MAX_LOCAL_EXPERTS + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = (wave / NWN) & 1, wn = wave % NWN;
     const int rr = lane & 15, g = lane >> 4;
     const int Kdim = kGemm1 ? p.H : p.I;
     const int KB = Kdim >> 7;
@@ -133,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
 
     // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
     // waits on a global load of its own
-    for (int i = tid; i <= p.El; i += kThreads) sOff[i] = p.pool_off[i];
+    for (int i = tid; i <= p.El; i += NW * 64) sOff[i] = p.pool_off[i];
     __syncthreads();
 
     // tile j of this work-group -> pool block, n tile and local expert (no holes: the last group of
@@ -157,65 +181,93 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
         }
         le = lo;
     };
+    // weight row (relative to the tile's first weight row) of B tile row r
+    auto b_row = [&](int r) { return kGemm1 ? (r < 128 ? r : p.I - 128 + r) : r; };
+    auto a_base = [&](int b) { return (kGemm1 ? p.pool_x : p.l2_x) + (size_t)b * BM * Kdim; };
+    auto w_base = [&](int le, int nt) {
+        return kGemm1 ? p.w1 + ((size_t)le * (2 * p.I) + nt * 128) * p.H : p.w2 + ((size_t)le * p.H + nt * 256) * p.I;
+    };
 
-    // per-lane parts of the DMA addresses (the same for every tile and step)
-    int a_off[A_INS], b_off[B_INS];
+    // per-lane DMA offsets (fixed for the whole kernel)
+    uint32_t a_off[A_INS], b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int r = (i * 8 + wave) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
         a_off[i] = r * Kdim + c * 16;
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-        const int r = (i * 8 + wave) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
-        const int wr = kGemm1 ? (r < 128 ? r : p.I - 128 + r) : r;     // + the tile's row base
-        b_off[i] = wr * Kdim + c * 16;
+        const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
+        b_off[i] = b_row(r) * Kdim + c * 16;
     }
-    const int sa_off = (wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * KB;
+    const uint32_t sa_off = (wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * KB * 4;
+    uint32_t meta_off[META_INS];
+#pragma unroll
+    for (int i = 0; i < META_INS; ++i) {
+        const int d = wave * META_PER_WAVE + i * 64 + lane;
+        meta_off[i] = (uint32_t)(lane + i * 64 < META_PER_WAVE ? d : 0) * 4;
+    }
 
-    // issue side: the step whose DMA goes out next, walked incrementally (tile ij, K step ikb)
-    int ij = 0, ikb = 0, ibuf = 0, ib = 0, int_ = 0, ile = 0;
-    tile_of(0, ib, int_, ile);
-    auto issue = [&]() {
-        const size_t row0 = (size_t)ib * BM;
-        const int kb = ikb, buf = ibuf, nt = int_, le = ile;
-        const uint8_t* A = (kGemm1 ? p.pool_x : p.l2_x) + row0 * Kdim + kb * 128;
-#pragma unroll
-        for (int i = 0; i < A_INS; ++i) dma16(A + a_off[i], &sA[buf][(i * 8 + wave) * 1024]);
-        const uint8_t* W = kGemm1 ? p.w1 + ((size_t)le * (2 * p.I) + nt * 128) * p.H
-                                  : p.w2 + ((size_t)le * p.H + nt * 256) * p.I;
-        W += kb * 128;
-#pragma unroll
-        for (int i = 0; i < B_INS; ++i) dma16(W + b_off[i], &sB[buf][(i * 8 + wave) * 1024]);
-        const float* Asf = (kGemm1 ? p.pool_sf : p.l2_sf) + row0 * KB + kb;
-        if (lane < SA_LANES) dma4(Asf + sa_off, &sSA[buf][wave * SA_LANES]);
-        const float* Wsf = kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
-                                  : p.w2_sf + (size_t)le * (p.H >> 7) * KB;
+    // issue side: the next step to load, tile ij and K step ikb; per-tile base pointers advance by one
+    // K step per issue
+    int ij = 0, ikb = 0;
+    const uint8_t* iA;
+    const uint8_t* iW;
+    const uint8_t* iAsf;
+    const uint8_t* iWsf;
+    const uint8_t* iMeta;
+    uint32_t sw_off = 0;
+    auto set_issue_tile = [&]() {
+        int b, nt, le;
+        tile_of(ij, b, nt, le);
+        const size_t row0 = (size_t)b * BM;
+        iA = a_base(b);
+        iW = w_base(le, nt);
+        iAsf = reinterpret_cast<const uint8_t*>((kGemm1 ? p.pool_sf : p.l2_sf) + row0 * KB);
+        iWsf = reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
+                                                       : p.w2_sf + (size_t)le * (p.H >> 7) * KB);
+        iMeta = reinterpret_cast<const uint8_t*>(p.pool_meta + row0 * 3);
         int blk;
         if (kGemm1) blk = lane == 0 ? nt : (p.I >> 7) + nt;          // gate block, up block
-        else blk = nt * 2 + (wn >> 1);
-        if (lane < 2) dma4(Wsf + (size_t)blk * KB + kb, &sSW[buf][wave][0]);
+        else blk = nt * 2 + (wn * WROWS) / 128;
+        sw_off = (uint32_t)(blk * KB) * 4;
+    };
+    set_issue_tile();
+    auto issue = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i) dma16(iA, a_off[i], &sA[buf][(i * NW + wave) * 1024]);
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i) dma16(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
+        if (lane < SA_LANES) dma4(iAsf, sa_off, &sSA[buf][wave * SA_LANES]);
+        if (lane < 2) dma4(iWsf, sw_off, &sSW[buf][wave][0]);
         if (!kGemm1) {
-            if (lane < META_LANES)
-                dma4(p.pool_meta + row0 * 3 + wave * META_LANES + lane, &sMeta[buf][wave * META_LANES]);
+#pragma unroll
+            for (int i = 0; i < META_INS; ++i)
+                if (lane + i * 64 < META_PER_WAVE)
+                    dma4(iMeta, meta_off[i], &sMeta[buf][wave * META_PER_WAVE + i * 64]);
         }
         // advance; past the last step the last step is loaded again (constant DMA count per step)
-        ibuf = ibuf == kStages - 1 ? 0 : ibuf + 1;
         if (ikb + 1 < KB) {
             ++ikb;
+            iA += 128;
+            iW += 128;
+            iAsf += 4;
+            iWsf += 4;
         } else if (ij + 1 < my_tiles) {
             ikb = 0;
             ++ij;
-            tile_of(ij, ib, int_, ile);
+            set_issue_tile();
         }
     };
 
-    // LDS row of this wave's weight subtile a
+    // LDS row of this wave's weight subtile a (GEMM1: the first WN/2 are gate rows, the rest the
+    // matching up rows, so gate and up of one output column sit in the same lane)
     int wrow0[WN];
 #pragma unroll
     for (int a = 0; a < WN; ++a) {
-        if (kGemm1) wrow0[a] = (a < 2 ? 0 : 128) + wn * 32 + (a & 1) * 16;
-        else wrow0[a] = wn * 64 + a * 16;
+        if (kGemm1) wrow0[a] = (a < WN / 2 ? 0 : 128) + wn * HC + (a % (WN / 2)) * 16;
+        else wrow0[a] = wn * WROWS + a * 16;
     }
 
     v4f acc[WN][TM];
@@ -224,54 +276,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    issue();
-    issue();
-    int cj = 0, ckb = 0, cbuf = 0;      // compute side: tile, K step, stage
-    for (int s = 0; s < nsteps; ++s) {
-        wait_stage_barrier<DMA_PER_STEP>();     // stage s landed in every wave; stage s-1 is free
-        issue();
-        const int buf = cbuf, kb = ckb, j = cj;
-        cbuf = cbuf == kStages - 1 ? 0 : cbuf + 1;
-        if (++ckb == KB) { ckb = 0; ++cj; }
+    int cj = 0, ckb = 0;      // compute side: tile and K step
 
-        const float sw0 = sSW[buf][wave][0], sw1 = sSW[buf][wave][1];
-        float sa[TM];
-        v8i xf[TM];
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const int r0 = wm * (BM / 2) + t * 16;
-            sa[t] = sSA[buf][r0 + rr];
-            xf[t] = load_frag(sA[buf], r0, lane);
-        }
-#pragma unroll
-        for (int a = 0; a < WN; ++a) {
-            const v8i wf = load_frag(sB[buf], wrow0[a], lane);
-            const float swa = (kGemm1 && a >= 2) ? sw1 : sw0;
-#pragma unroll
-            for (int t = 0; t < TM; ++t) {
-                const v4f pr = mfma_fp8(wf, xf[t], v4f{0.f, 0.f, 0.f, 0.f});
-                acc[a][t] += (sa[t] * swa) * pr;
-            }
-        }
-        if (kb != KB - 1) continue;
-
-        // ------------------------------------------------------------------ epilogue of tile j
+    auto epilogue = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         // lane holds acc[a][t][i]: weight row wrow0[a] + 4g + i, token wm*BM/2 + 16t + rr
         int b, nt, le_unused;
-        tile_of(j, b, nt, le_unused);
+        tile_of(cj, b, nt, le_unused);
         (void)le_unused;
         const size_t row0 = (size_t)b * BM;
         if (kGemm1) {
-            float h[2][TM][4];
+            constexpr int HA = WN / 2;
+            float h[HA][TM][4];
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 float m = 0.f;
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                for (int a = 0; a < HA; ++a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float gt = acc[a][t][i], up = acc[a + 2][t][i];
-                        const float v = gt / (1.0f + __expf(-gt)) * up;
+                        const float gt = acc[a][t][i], up = acc[a + HA][t][i];
+                        const float v = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
                         h[a][t][i] = v;
                         m = fmaxf(m, fabsf(v));
                     }
@@ -284,20 +309,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 const int tok = wm * (BM / 2) + t * 16 + rr;
-                const float* red = sRed[tok];
-                const float am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+                float am = sRed[tok][0];
+#pragma unroll
+                for (int w = 1; w < NWN; ++w) am = fmaxf(am, sRed[tok][w]);
                 const float sc = fmaxf(am, 1e-4f) / 448.0f;
                 const size_t row = row0 + tok;
 #pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    const int col = nt * 128 + wn * 32 + a * 16 + 4 * g;
+                for (int a = 0; a < HA; ++a) {
+                    const int col = nt * 128 + wn * HC + a * 16 + 4 * g;
                     const uint32_t q = cvt_fp8x4(h[a][t][0] / sc, h[a][t][1] / sc, h[a][t][2] / sc,
                                                  h[a][t][3] / sc);
                     *reinterpret_cast<uint32_t*>(p.l2_x + row * I + col) = q;
                     if (p.gemm1_out) {
                         float* go = p.gemm1_out + row * (size_t)(2 * I);
                         *reinterpret_cast<v4f*>(go + col) = acc[a][t];
-                        *reinterpret_cast<v4f*>(go + I + col) = acc[a + 2][t];
+                        *reinterpret_cast<v4f*>(go + I + col) = acc[a + HA][t];
                     }
                 }
                 if (wn == 0 && g == 0) p.l2_sf[row * (size_t)(I >> 7) + nt] = sc;
@@ -314,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
                 uint16_t* dst = p.comb + ((size_t)mk * plane + (size_t)ms * p.T_max + mt) * p.H;
 #pragma unroll
                 for (int a = 0; a < WN; ++a) {
-                    const int col = nt * 256 + wn * 64 + a * 16 + 4 * g;
+                    const int col = nt * 256 + wn * WROWS + a * 16 + 4 * g;
                     uint2 v;
                     v.x = (uint32_t)f32_to_bf16(acc[a][t][0]) | ((uint32_t)f32_to_bf16(acc[a][t][1]) << 16);
                     v.y = (uint32_t)f32_to_bf16(acc[a][t][2]) | ((uint32_t)f32_to_bf16(acc[a][t][3]) << 16);
@@ -326,6 +352,60 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
         for (int a = 0; a < WN; ++a)
 #pragma unroll
             for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // one K step on stage buf: wait for it, refill the stage two steps ahead, MFMAs with the
+    // promotion pipelined two MFMAs behind, and the epilogue after a tile's last step
+    auto step = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        wait_vm_barrier<DMA_PER_STEP>();        // this stage landed in every wave; stage buf-1 is free
+        issue(ic<(buf + 2) % kStages>{});
+        // promotion factors: token scale x the wave's weight-block scale (GEMM1: gate and up blocks)
+        constexpr int NSW = kGemm1 ? 2 : 1;
+        float sc[NSW][TM];
+        {
+            const float sw0 = sSW[buf][wave][0], sw1 = sSW[buf][wave][1];
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                const float sa = sSA[buf][wm * (BM / 2) + t * 16 + rr];
+                sc[0][t] = sa * sw0;
+                if (kGemm1) sc[NSW - 1][t] = sa * sw1;
+            }
+        }
+        v8i xf[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) xf[t] = load_frag(sA[buf], wm * (BM / 2) + t * 16, lane);
+        v8i wf[2];
+        wf[0] = load_frag(sB[buf], wrow0[0], lane);
+        v4f pr[3];
+#pragma unroll
+        for (int i = 0; i < NMF + 2; ++i) {
+            if (i < NMF) {
+                const int a = i / TM, t = i % TM;
+                if (t == 0 && a + 1 < WN) wf[(a + 1) & 1] = load_frag(sB[buf], wrow0[a + 1], lane);
+                pr[i % 3] = mfma_fp8(wf[a & 1], xf[t], v4f{0.f, 0.f, 0.f, 0.f});
+            }
+            if (i >= 2) {
+                const int k = i - 2, a = k / TM, t = k % TM;
+                const int si = (kGemm1 && a >= WN / 2) ? NSW - 1 : 0;
+                acc[a][t] += sc[si][t] * pr[k % 3];
+            }
+        }
+        if (++ckb == KB) {
+            epilogue(bufc);
+            ckb = 0;
+            ++cj;
+        }
+    };
+
+    issue(ic<0>{});
+    issue(ic<1>{});
+    for (int s = 0; s < nsteps; s += kStages) {
+        step(ic<0>{});
+        if (s + 1 >= nsteps) break;
+        step(ic<1>{});
+        if (s + 2 >= nsteps) break;
+        step(ic<2>{});
     }
     wait_all_vm();      // no LDS DMA may still be landing when the work-group ends
 }
@@ -333,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
 template <int BM, bool kGemm1>
 hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     int grid = (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kGemm1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
     return hipGetLastError();
 }
 
