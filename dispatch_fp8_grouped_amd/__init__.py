@@ -61,7 +61,7 @@ class mega_moe_config(ctypes.Structure):
 
 
 _LAYOUT_U64 = ("status", "chunk_hist", "chunk_base", "send", "recv", "recv_tot", "pool_off", "block_expert",
-               "block_index", "table", "pool_x", "pool_sf", "pool_meta", "l2_x", "l2_sf", "comb", "gemm1_out",
+               "block_index", "table", "pool_x", "pool_sf", "pool_meta", "pool_dst", "l2_x", "l2_sf", "comb", "gemm1_out",
                "total")
 
 

@@ -7,8 +7,9 @@
 // alternate between the active sources in ascending order.  One lane per source runs the rounds with
 // wave ballots and a wave-wide minimum.  The table entry t*K+k at (le, source, slot) names the token;
 // its H-byte row, its H/128 scales and the metadata {shard, token, k} are copied
-// ("Mega-MoE notes, part 2", 2.6; "Dispatch/Combine ... comparison", 6.2).  Rows past the expert's
-// count are padding: zero codes, zero scales, metadata all ones.
+// ("Mega-MoE notes, part 2", 2.6; "Dispatch/Combine ... comparison", 6.2), with the row's GEMM2
+// scatter target k*S*T_max + shard*T_max + token beside them.  Rows past the expert's count are
+// padding: zero codes, zero scales, metadata and target all ones.
 //
 // One wave per pool row, 16-byte loads and stores, all loads of a row issued before its stores.
 #include "mm_internal.h"
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
             for (int i = lane; i < H16; i += 64) dst[i] = z;
             for (int i = lane; i < SF; i += 64) dsf[i] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
+            if (lane == 3) p.pool_dst[row] = kMetaPad;
             continue;
         }
         // min-peeling round-robin over the sources (lane = source shard).  Every round retires at
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
             for (int i = lane; i < H16; i += 64) dst[i] = v4i{0, 0, 0, 0};
             for (int i = lane; i < SF; i += 64) dsf[i] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
+            if (lane == 3) p.pool_dst[row] = kMetaPad;
             continue;
         }
         const int t = v / p.K, k = v - t * p.K;
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
         const float* ssf = p.x_sf + srow * SF;
         for (int i = lane; i < SF; i += 64) dsf[i] = ssf[i];
         if (lane < 3) meta[lane] = lane == 0 ? (uint32_t)src : (lane == 1 ? (uint32_t)t : (uint32_t)k);
+        if (lane == 3) p.pool_dst[row] = (uint32_t)(((size_t)k * p.S + src) * p.T_max + t);
     }
 }
 

@@ -58,12 +58,13 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + (swz_chunk(r
 
 // Fragment of 16 rows x 128 K bytes for one MFMA operand: lane l takes row (l & 15) and the 32 bytes
 // [32*(l>>4), +32).  A and B use the same lane -> K mapping, so the product sums every K exactly once.
-__device__ __forceinline__ v8i load_frag(const uint8_t* lds, int row0, int lane) {
-    const int r = row0 + (lane & 15);
-    const int g = lane >> 4;
-    const v4i lo = *reinterpret_cast<const v4i*>(lds + swz(r, 2 * g));
-    const v4i hi = *reinterpret_cast<const v4i*>(lds + swz(r, 2 * g + 1));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// lo / hi point at the lane's two 16-byte chunks in the first fragment row block; fragments whose first
+// row differs by a multiple of 16 (and other stages) sit at a constant byte offset from them, since the
+// swizzle depends on the row's low four bits only.
+__device__ __forceinline__ v8i load_frag(const uint8_t* lo, const uint8_t* hi, int off) {
+    const v4i a = *reinterpret_cast<const v4i*>(lo + off);
+    const v4i b = *reinterpret_cast<const v4i*>(hi + off);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Four fp32 -> four e4m3fn codes (round to nearest even, saturating), byte i from value i.  The
@@ -76,8 +77,8 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(float a, float b, float c, float d
     return (uint32_t)v;
 }
 
-// LDS DMA: every active lane copies 16 (or 4) bytes from base + off to LDS at dst + lane * size (dst and
-// base wave-uniform, off per lane).  Inline asm: the waits for these writes are placed by hand
+// LDS DMA: every lane copies 16 bytes from base + off (or 4 bytes from its own address) to LDS at
+// dst + lane * size (dst and base wave-uniform, off per lane).  Inline asm: the waits for these writes are placed by hand
 // (wait_stage_barrier); the compiler, which cannot tell the three stages apart, would otherwise drain
 // every DMA in flight before each LDS read.  M0 is set in the same statement.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -94,17 +95,19 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, const void
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, const void* dst) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-                 :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
+// 4 bytes per lane from a per-lane address (every lane active)
+__device__ __forceinline__ void dma4_lane(const void* src, const void* dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding, then barrier.  The
-// compiler's __syncthreads would drain every LDS DMA in flight; this keeps the younger stage loading.
+// Wait until at most N vector-memory operations of this wave are outstanding and its LDS reads have
+// returned, then barrier.  The compiler's __syncthreads would drain every LDS DMA in flight; this keeps
+// the younger stage loading.
 template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
+__device__ __forceinline__ void wait_stage_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt immediate");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -123,18 +126,16 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int NMF = TM * WN;                // MFMAs per wave and K step
     constexpr int A_INS = BM / (8 * NW);        // 1 KB A DMA instructions per wave and step
     constexpr int B_INS = 32 / NW;              // 1 KB B DMA instructions per wave and step
-    constexpr int SA_LANES = BM / NW;           // token scales per wave and step
-    constexpr int META_PER_WAVE = BM * 3 / NW;  // metadata dwords per wave and step (GEMM2)
-    constexpr int META_INS = (META_PER_WAVE + 63) / 64;
-    constexpr int DMA_PER_STEP = A_INS + B_INS + 2 + (kGemm1 ? 0 : META_INS);
-    static_assert(A_INS >= 1 && B_INS >= 1 && SA_LANES <= 64, "tile shape");
+    constexpr int SA_LANES = BM / NW;           // token rows whose scale (and GEMM2 target) a wave loads
+    constexpr int DMA_PER_STEP = A_INS + B_INS + 1;
+    static_assert(A_INS >= 1 && B_INS >= 1 && 2 * SA_LANES + 2 <= 64, "tile shape");
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * 128];
-    __shared__ __attribute__((aligned(16))) float sSA[kStages][BM];
-    __shared__ __attribute__((aligned(16))) float sSW[kStages][NW][4];
-    __shared__ __attribute__((aligned(16))) uint32_t sMeta[kStages][kGemm1 ? 4 : META_INS * 64 * NW];
+    // per stage and wave, 64 dwords written by one DMA: [0, SA_LANES) token scales of rows
+    // wave*SA_LANES + l, then the wave's two weight-block scales, then (GEMM2) the rows' scatter targets
+    __shared__ __attribute__((aligned(16))) uint32_t sSmall[kStages][NW * 64];
     __shared__ float sRed[BM][NWN];
     __shared__ int sOff[MEGA_MOE_MAX_LOCAL_EXPERTS + 1];
 
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 
     // tile j of this work-group -> pool block, n tile and local expert (no holes: the last group of
     // blocks may be short)
-    auto tile_of = [&](int j, int& b, int& nt, int& le) {
+    auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
         const int t = logical + j * G;
         if (t < full) {
             const int grp = t / (kGroupBlocks * NT);
@@ -200,60 +201,51 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
         b_off[i] = b_row(r) * Kdim + c * 16;
     }
-    const uint32_t sa_off = (wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * KB * 4;
-    uint32_t meta_off[META_INS];
-#pragma unroll
-    for (int i = 0; i < META_INS; ++i) {
-        const int d = wave * META_PER_WAVE + i * 64 + lane;
-        meta_off[i] = (uint32_t)(lane + i * 64 < META_PER_WAVE ? d : 0) * 4;
-    }
+    // lane role in the small DMA: token scale of row wave*SA_LANES + l, weight-block scale j, or
+    // (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes repeat lane 0's load
+    const int sm_role = lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? 1 : (!kGemm1 && lane < 2 * SA_LANES + 2) ? 2 : 3;
+    const int sm_row = wave * SA_LANES + (sm_role == 0 ? lane : sm_role == 2 ? lane - SA_LANES - 2 : 0);
+    const uint32_t sm_inc = sm_role == 2 ? 0u : 4u;     // bytes per K step
 
-    // issue side: the next step to load, tile ij and K step ikb; per-tile base pointers advance by one
-    // K step per issue
+    // issue side: the next step to load, tile ij and K step ikb; the base pointers advance by one K
+    // step per issue
     int ij = 0, ikb = 0;
     const uint8_t* iA;
     const uint8_t* iW;
-    const uint8_t* iAsf;
-    const uint8_t* iWsf;
-    const uint8_t* iMeta;
-    uint32_t sw_off = 0;
-    auto set_issue_tile = [&]() {
+    const uint8_t* iSm;     // per lane
+    auto set_issue_tile = [&]() __attribute__((always_inline)) {
         int b, nt, le;
         tile_of(ij, b, nt, le);
         const size_t row0 = (size_t)b * BM;
         iA = a_base(b);
         iW = w_base(le, nt);
-        iAsf = reinterpret_cast<const uint8_t*>((kGemm1 ? p.pool_sf : p.l2_sf) + row0 * KB);
-        iWsf = reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
-                                                       : p.w2_sf + (size_t)le * (p.H >> 7) * KB);
-        iMeta = reinterpret_cast<const uint8_t*>(p.pool_meta + row0 * 3);
+        const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (row0 + sm_row) * KB;
         int blk;
-        if (kGemm1) blk = lane == 0 ? nt : (p.I >> 7) + nt;          // gate block, up block
+        if (kGemm1) blk = lane == SA_LANES ? nt : (p.I >> 7) + nt;     // gate block, up block
         else blk = nt * 2 + (wn * WROWS) / 128;
-        sw_off = (uint32_t)(blk * KB) * 4;
+        const float* wsf = (kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
+                                   : p.w2_sf + (size_t)le * (p.H >> 7) * KB) + (size_t)blk * KB;
+        const uint32_t* dst = p.pool_dst + row0 + sm_row;
+        iSm = sm_role == 1 ? reinterpret_cast<const uint8_t*>(wsf)
+            : sm_role == 2 ? reinterpret_cast<const uint8_t*>(dst) : reinterpret_cast<const uint8_t*>(asf);
     };
     set_issue_tile();
-    auto issue = [&](auto bufc) {
+    // the DMA of one K step into stage buf: straight-line code, every lane active
+    auto issue_dma = [&](auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) dma16(iA, a_off[i], &sA[buf][(i * NW + wave) * 1024]);
 #pragma unroll
         for (int i = 0; i < B_INS; ++i) dma16(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
-        if (lane < SA_LANES) dma4(iAsf, sa_off, &sSA[buf][wave * SA_LANES]);
-        if (lane < 2) dma4(iWsf, sw_off, &sSW[buf][wave][0]);
-        if (!kGemm1) {
-#pragma unroll
-            for (int i = 0; i < META_INS; ++i)
-                if (lane + i * 64 < META_PER_WAVE)
-                    dma4(iMeta, meta_off[i], &sMeta[buf][wave * META_PER_WAVE + i * 64]);
-        }
-        // advance; past the last step the last step is loaded again (constant DMA count per step)
+        dma4_lane(iSm, &sSmall[buf][wave * 64]);
+    };
+    // advance to the next step; past the last step the last step is loaded again (constant DMA count)
+    auto issue_advance = [&]() __attribute__((always_inline)) {
         if (ikb + 1 < KB) {
             ++ikb;
             iA += 128;
             iW += 128;
-            iAsf += 4;
-            iWsf += 4;
+            iSm += sm_inc;
         } else if (ij + 1 < my_tiles) {
             ikb = 0;
             ++ij;
@@ -261,14 +253,51 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         }
     };
 
-    // LDS row of this wave's weight subtile a (GEMM1: the first WN/2 are gate rows, the rest the
-    // matching up rows, so gate and up of one output column sit in the same lane)
-    int wrow0[WN];
+    // LDS row of this wave's weight subtile a relative to the wave's first weight row (GEMM1: the
+    // first WN/2 are gate rows, the rest the matching up rows, so gate and up of one output column sit
+    // in the same lane), and the lane's fragment chunk pointers
+    auto wrow = [](int a) { return kGemm1 ? (a < WN / 2 ? 0 : 128) + (a % (WN / 2)) * 16 : a * 16; };
+    const int xr = wm * (BM / 2) + rr;
+    const int wr = (kGemm1 ? wn * HC : wn * WROWS) + rr;
+    const uint8_t* xlo = &sA[0][0] + swz(xr, 2 * g);
+    const uint8_t* xhi = &sA[0][0] + swz(xr, 2 * g + 1);
+    const uint8_t* wlo = &sB[0][0] + swz(wr, 2 * g);
+    const uint8_t* whi = &sB[0][0] + swz(wr, 2 * g + 1);
+
+    // One K step's operands in registers: token and weight fragments, the promotion factors (token
+    // scale x weight-block scale; GEMM1 has a gate and an up block) and, for GEMM2, the scatter target
+    // of the wave's tokens (needed after the stage itself has been refilled).  load_head reads all but
+    // the second half of the weight fragments, which load_tail reads during the step's first half.
+    constexpr int NSW = kGemm1 ? 2 : 1;
+    struct Frags {
+        v8i x[TM];
+        v8i w[WN];
+        float sc[NSW][TM];
+        uint32_t dst[kGemm1 ? 1 : TM];
+    };
+    auto load_head = [&](Frags& f, auto bufc) __attribute__((always_inline)) {
+        constexpr int buf = decltype(bufc)::value;
+        const float sw0 = __uint_as_float(sSmall[buf][wave * 64 + SA_LANES]);
+        const float sw1 = __uint_as_float(sSmall[buf][wave * 64 + SA_LANES + 1]);
 #pragma unroll
-    for (int a = 0; a < WN; ++a) {
-        if (kGemm1) wrow0[a] = (a < WN / 2 ? 0 : 128) + wn * HC + (a % (WN / 2)) * 16;
-        else wrow0[a] = wn * WROWS + a * 16;
-    }
+        for (int t = 0; t < TM; ++t) {
+            const int r = wm * (BM / 2) + t * 16 + rr;          // token row; loaded by wave r / SA_LANES
+            const int slot = (r / SA_LANES) * 64 + r % SA_LANES;
+            const float sa = __uint_as_float(sSmall[buf][slot]);
+            f.sc[0][t] = sa * sw0;
+            if (kGemm1) f.sc[NSW - 1][t] = sa * sw1;
+            if (!kGemm1) f.dst[kGemm1 ? 0 : t] = sSmall[buf][slot + SA_LANES + 2];
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) f.x[t] = load_frag(xlo, xhi, buf * BM * 128 + t * 16 * 128);
+#pragma unroll
+        for (int a = 0; a < WN / 2; ++a) f.w[a] = load_frag(wlo, whi, buf * 256 * 128 + wrow(a) * 128);
+    };
+    auto load_tail = [&](Frags& f, auto bufc) __attribute__((always_inline)) {
+        constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+        for (int a = WN / 2; a < WN; ++a) f.w[a] = load_frag(wlo, whi, buf * 256 * 128 + wrow(a) * 128);
+    };
 
     v4f acc[WN][TM];
 #pragma unroll
@@ -278,9 +307,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 
     int cj = 0, ckb = 0;      // compute side: tile and K step
 
-    auto epilogue = [&](auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        // lane holds acc[a][t][i]: weight row wrow0[a] + 4g + i, token wm*BM/2 + 16t + rr
+    auto epilogue = [&](const Frags& f) __attribute__((always_inline)) {
+        // lane holds acc[a][t][i]: weight row wr - rr + wrow(a) + 4g + i, token wm*BM/2 + 16t + rr
         int b, nt, le_unused;
         tile_of(cj, b, nt, le_unused);
         (void)le_unused;
@@ -330,14 +358,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             }
             lds_barrier();      // sRed is rewritten by the next tile
         } else {
-            const size_t plane = (size_t)p.S * p.T_max;
-            const uint32_t* meta = sMeta[buf];
+            const uint32_t comb_rows = (uint32_t)(p.K * p.S * p.T_max);
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                const int tok = wm * (BM / 2) + t * 16 + rr;
-                const uint32_t ms = meta[tok * 3], mt = meta[tok * 3 + 1], mk = meta[tok * 3 + 2];
-                if (ms >= (uint32_t)p.S || mt >= (uint32_t)p.T_max || mk >= (uint32_t)p.K) continue;  // padding
-                uint16_t* dst = p.comb + ((size_t)mk * plane + (size_t)ms * p.T_max + mt) * p.H;
+                const uint32_t d = f.dst[kGemm1 ? 0 : t];
+                if (d >= comb_rows) continue;       // padding (all ones)
+                uint16_t* dst = p.comb + (size_t)d * p.H;
 #pragma unroll
                 for (int a = 0; a < WN; ++a) {
                     const int col = nt * 256 + wn * WROWS + a * 16 + 4 * g;
@@ -354,58 +380,98 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
     };
 
-    // one K step on stage buf: wait for it, refill the stage two steps ahead, MFMAs with the
-    // promotion pipelined two MFMAs behind, and the epilogue after a tile's last step
-    auto step = [&](auto bufc) {
+    // Promotion of MFMA k runs kLag MFMAs after it was issued (a ring of kRing products), so the
+    // VALU never waits on the matrix core; the last kLag promotions of a step run at the start of
+    // the next one, with the previous step's factors.
+    constexpr int kLag = 2, kRing = 4;
+    static_assert(NMF % kRing == 0 && kLag < kRing && kLag <= NMF / 2, "promotion ring");
+    v4f P[kRing];
+    Frags F[2];
+    auto promote = [&](const Frags& f, int k) __attribute__((always_inline)) {
+        const int a = k / TM, t = k % TM;
+        const int si = (kGemm1 && a >= WN / 2) ? NSW - 1 : 0;
+        acc[a][t] += f.sc[si][t] * P[k % kRing];
+    };
+    // LDS reads of load_tail (first half) and load_head (second half), spread over the MFMAs
+    constexpr int DS_TAIL = (WN + NMF / 2 - 1) / (NMF / 2);
+    constexpr int DS_HEAD = (2 * TM + WN + TM + 2 + (kGemm1 ? 0 : TM) + NMF / 2 - 1) / (NMF / 2);
+
+    // One K step s on stage buf, operands in F[par] (read during step s-1).  Half-way through, after
+    // the wait for stage s+1 and a barrier (every wave has finished reading stage s by then), stage
+    // buf is refilled with step s+3 and the operands of step s+1 are read into F[par ^ 1] while the
+    // second half's MFMAs run.  After a tile's last step: the pending promotions, then the epilogue.
+    auto step = [&](auto bufc, auto parc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
-        wait_vm_barrier<DMA_PER_STEP>();        // this stage landed in every wave; stage buf-1 is free
-        issue(ic<(buf + 2) % kStages>{});
-        // promotion factors: token scale x the wave's weight-block scale (GEMM1: gate and up blocks)
-        constexpr int NSW = kGemm1 ? 2 : 1;
-        float sc[NSW][TM];
-        {
-            const float sw0 = sSW[buf][wave][0], sw1 = sSW[buf][wave][1];
+        constexpr int par = decltype(parc)::value;
+        Frags& fc = F[par];
+        Frags& fn = F[par ^ 1];
 #pragma unroll
-            for (int t = 0; t < TM; ++t) {
-                const float sa = sSA[buf][wm * (BM / 2) + t * 16 + rr];
-                sc[0][t] = sa * sw0;
-                if (kGemm1) sc[NSW - 1][t] = sa * sw1;
+        for (int i = 0; i < NMF; ++i) {
+            if (i == 0) load_tail(fc, bufc);
+            if (i == NMF / 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                wait_stage_barrier<DMA_PER_STEP>();
+                __builtin_amdgcn_sched_barrier(0);
+                issue_dma(ic<buf>{});
+                load_head(fn, ic<(buf + 1) % kStages>{});
             }
+            P[i % kRing] = mfma_fp8(fc.w[i / TM], fc.x[i % TM], v4f{0.f, 0.f, 0.f, 0.f});
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+            if (i >= kLag) promote(fc, i - kLag);
+            else promote(fn, NMF + i - kLag);                        // previous step's last MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // its promotion on VALU
+            if (i < NMF / 2) __builtin_amdgcn_sched_group_barrier(0x100, DS_TAIL, 0);      // LDS reads
+            else __builtin_amdgcn_sched_group_barrier(0x100, DS_HEAD, 0);
         }
-        v8i xf[TM];
+        // keep this step's promotions inside the step's block, where the schedule interleaves them
+        // with the MFMAs (otherwise they may be sunk past the branches below)
 #pragma unroll
-        for (int t = 0; t < TM; ++t) xf[t] = load_frag(sA[buf], wm * (BM / 2) + t * 16, lane);
-        v8i wf[2];
-        wf[0] = load_frag(sB[buf], wrow0[0], lane);
-        v4f pr[3];
+        for (int a = 0; a < WN; ++a)
 #pragma unroll
-        for (int i = 0; i < NMF + 2; ++i) {
-            if (i < NMF) {
-                const int a = i / TM, t = i % TM;
-                if (t == 0 && a + 1 < WN) wf[(a + 1) & 1] = load_frag(sB[buf], wrow0[a + 1], lane);
-                pr[i % 3] = mfma_fp8(wf[a & 1], xf[t], v4f{0.f, 0.f, 0.f, 0.f});
-            }
-            if (i >= 2) {
-                const int k = i - 2, a = k / TM, t = k % TM;
-                const int si = (kGemm1 && a >= WN / 2) ? NSW - 1 : 0;
-                acc[a][t] += sc[si][t] * pr[k % 3];
-            }
-        }
+            for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(acc[a][t]));
+        issue_advance();
         if (++ckb == KB) {
-            epilogue(bufc);
+#pragma unroll
+            for (int k = NMF - kLag; k < NMF; ++k) {
+                promote(fc, k);
+                P[k % kRing] = v4f{0.f, 0.f, 0.f, 0.f};   // the next step's catch-up adds zero
+            }
+#pragma unroll
+            for (int j = 0; j < NSW; ++j)
+#pragma unroll
+                for (int t = 0; t < TM; ++t) fc.sc[j][t] = 0.f;
+            epilogue(fc);
             ckb = 0;
             ++cj;
         }
     };
 
-    issue(ic<0>{});
-    issue(ic<1>{});
-    for (int s = 0; s < nsteps; s += kStages) {
-        step(ic<0>{});
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) P[k] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NSW; ++j)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) F[1].sc[j][t] = 0.f;
+    issue_dma(ic<0>{});
+    issue_advance();
+    issue_dma(ic<1>{});
+    issue_advance();
+    issue_dma(ic<2>{});
+    issue_advance();
+    wait_stage_barrier<2 * DMA_PER_STEP>();
+    load_head(F[0], ic<0>{});
+    for (int s = 0; s < nsteps; s += 2 * kStages) {
+        step(ic<0>{}, ic<0>{});
         if (s + 1 >= nsteps) break;
-        step(ic<1>{});
+        step(ic<1>{}, ic<1>{});
         if (s + 2 >= nsteps) break;
-        step(ic<2>{});
+        step(ic<2>{}, ic<0>{});
+        if (s + 3 >= nsteps) break;
+        step(ic<0>{}, ic<1>{});
+        if (s + 4 >= nsteps) break;
+        step(ic<1>{}, ic<0>{});
+        if (s + 5 >= nsteps) break;
+        step(ic<2>{}, ic<1>{});
     }
     wait_all_vm();      // no LDS DMA may still be landing when the work-group ends
 }

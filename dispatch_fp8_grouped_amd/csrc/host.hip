@@ -96,6 +96,7 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->pool_x = take(rows * H);
     L->pool_sf = take(rows * (H / 128) * 4);
     L->pool_meta = take(rows * 3 * 4);
+    L->pool_dst = take(rows * 4);
     L->l2_x = take(rows * I);
     L->l2_sf = take(rows * (I / 128) * 4);
     L->comb = take(K * S * T * H * 2);
@@ -237,6 +238,7 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
     p.pool_x = w + L.pool_x;
     p.pool_sf = reinterpret_cast<float*>(w + L.pool_sf);
     p.pool_meta = reinterpret_cast<uint32_t*>(w + L.pool_meta);
+    p.pool_dst = reinterpret_cast<uint32_t*>(w + L.pool_dst);
     p.l2_x = w + L.l2_x;
     p.l2_sf = reinterpret_cast<float*>(w + L.l2_sf);
     p.comb = reinterpret_cast<uint16_t*>(w + L.comb);

@@ -35,6 +35,7 @@ struct Params {
     uint8_t* pool_x;      // [rows][H]
     float* pool_sf;       // [rows][H/128]
     uint32_t* pool_meta;  // [rows][3]
+    uint32_t* pool_dst;   // [rows]: comb row k*S*T_max + shard*T_max + token, padding ~0
     uint8_t* l2_x;        // [rows][I]
     float* l2_sf;         // [rows][I/128]
     uint16_t* comb;       // [K][S*T_max][H]

@@ -100,6 +100,8 @@ typedef struct mega_moe_layout {
     uint64_t pool_x;          /* uint8 [max_pool_blocks*BM][H] e4m3fn                              */
     uint64_t pool_sf;         /* float [max_pool_blocks*BM][H/128]                                 */
     uint64_t pool_meta;       /* uint32 [max_pool_blocks*BM][3] = {shard, token, k}; padding = ~0  */
+    uint64_t pool_dst;        /* uint32 [max_pool_blocks*BM]: comb row k*S*T_max + shard*T_max +   */
+                              /*   token of the pool row (the GEMM2 scatter target); padding = ~0  */
     uint64_t l2_x;            /* uint8 [max_pool_blocks*BM][I] e4m3fn                              */
     uint64_t l2_sf;           /* float [max_pool_blocks*BM][I/128]                                 */
     uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only        */

@@ -65,6 +65,11 @@ class Run:
         pm = self.region("pool_meta", torch.int32, (cap, 3))[sel].cpu().numpy().view(np.uint32)
         return px, psf, pm
 
+    def pool_dst_host(self):
+        nb = int(self.region("status", torch.int32, (2,))[1].item())
+        cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
+        return self.region("pool_dst", torch.int32, (cap,))[:nb * self.moe.block_m].cpu().numpy().view(np.uint32)
+
     def l2_host(self, rows):
         sh = self.shape
         cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
@@ -110,6 +115,11 @@ def check_layout(run, inp_np, ref=None):
     gx, gsf, gm = run.pool_host()
     assert gx.shape == px.shape
     assert np.array_equal(gm, pm), "pool metadata"
+    # scatter target of each pool row: comb row k*S*T_max + shard*T_max + token, padding all ones
+    pad = pm[:, 0] == 0xFFFFFFFF
+    want_dst = np.where(pad, np.uint64(0xFFFFFFFF),
+                        (pm[:, 2].astype(np.uint64) * sh.num_shards + pm[:, 0]) * sh.max_tokens_per_shard + pm[:, 1])
+    assert np.array_equal(run.pool_dst_host().astype(np.uint64), want_dst), "pool scatter targets"
     assert np.array_equal(gx, px), "pool rows"
     assert np.array_equal(gsf.view(np.uint32), psf.view(np.uint32)), "pool scales"
     return rt, off
