@@ -41,12 +41,13 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
         const int j = p.block_index[b] * p.BM + (int)(row - (long)b * p.BM);
         const int n = p.recv_tot[le];
         v4i* dst = reinterpret_cast<v4i*>(p.pool_x + (size_t)row * p.H);
-        float* dsf = p.pool_sf + (size_t)row * SF;
+        // scales are block-major: K block i of this row at dsf[i * BM]
+        float* dsf = p.pool_sf + (size_t)b * SF * p.BM + (row - (long)b * p.BM);
         uint32_t* meta = p.pool_meta + (size_t)row * 3;
         if (j >= n) {
             const v4i z = {0, 0, 0, 0};
             for (int i = lane; i < H16; i += 64) dst[i] = z;
-            for (int i = lane; i < SF; i += 64) dsf[i] = 0.f;
+            for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
             if (lane == 3) p.pool_dst[row] = kMetaPad;
             continue;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
         if (v < 0 || v >= p.tps[src] * p.K) {              // never for metadata the routing stage made
             if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
             for (int i = lane; i < H16; i += 64) dst[i] = v4i{0, 0, 0, 0};
-            for (int i = lane; i < SF; i += 64) dsf[i] = 0.f;
+            for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
             if (lane == 3) p.pool_dst[row] = kMetaPad;
             continue;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
             }
         }
         const float* ssf = p.x_sf + srow * SF;
-        for (int i = lane; i < SF; i += 64) dsf[i] = ssf[i];
+        for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = ssf[i];
         if (lane < 3) meta[lane] = lane == 0 ? (uint32_t)src : (lane == 1 ? (uint32_t)t : (uint32_t)k);
         if (lane == 3) p.pool_dst[row] = (uint32_t)(((size_t)k * p.S + src) * p.T_max + t);
     }

@@ -27,8 +27,8 @@
 // tile's last ones.  Every step issues the same number of DMA instructions (past the end the last step
 // is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
 // XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
-// Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of a group of eight
-// pool blocks, which share A and B through that XCD's L2.
+// Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of one expert (eight
+// pool blocks x four n tiles), which share A and B through that XCD's L2.
 #include <type_traits>
 
 #include "mm_internal.h"
@@ -43,7 +43,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
 constexpr int kStages = 3;
-constexpr int kGroupBlocks = 8;   // pool blocks per tile group
+constexpr int kNtGroup = 4;       // n tiles per tile group
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // scale operands 0 select the unscaled v_mfma_f32_16x16x128_f8f6f4; format 0 = FP8 e4m3
@@ -153,34 +153,42 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     if (logical >= ntiles) return;
     const int my_tiles = (ntiles - 1 - logical) / G + 1;
     const int nsteps = my_tiles * KB;
-    const int full = (nblocks / kGroupBlocks) * kGroupBlocks * NT;
-    const int tail = nblocks % kGroupBlocks;
 
     // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
     // waits on a global load of its own
     for (int i = tid; i <= p.El; i += NW * 64) sOff[i] = p.pool_off[i];
     __syncthreads();
 
-    // tile j of this work-group -> pool block, n tile and local expert (no holes: the last group of
-    // blocks may be short)
+    // Tile t -> pool block, n tile and local expert.  Tiles are numbered expert by expert (expert le
+    // owns tiles [off[le]*NT, off[le+1]*NT)); inside an expert, by group of kNtGroup n tiles, then by
+    // block, then by n tile of the group.  A run of 32 consecutive tiles (one XCD's share of a round)
+    // is then 8 blocks x 4 n tiles of one expert: its A and W chunks are shared through that XCD's L2,
+    // and an expert's weights are fetched by about one XCD.
     auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
         const int t = logical + j * G;
-        if (t < full) {
-            const int grp = t / (kGroupBlocks * NT);
-            const int rem = t - grp * (kGroupBlocks * NT);
-            nt = rem / kGroupBlocks;
-            b = grp * kGroupBlocks + (rem - nt * kGroupBlocks);
-        } else {
-            const int rem = t - full;
-            nt = rem / tail;
-            b = full / NT + (rem - nt * tail);
-        }
-        int lo = 0, hi = p.El;              // last expert whose first block is <= b
+        const int vb = t / NT;
+        int lo = 0, hi = p.El;              // the expert with off[le] <= vb < off[le+1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (sOff[mid] <= b) lo = mid; else hi = mid;
+            if (sOff[mid] <= vb) lo = mid; else hi = mid;
         }
         le = lo;
+        const int b0 = sOff[lo], nb = max(sOff[lo + 1] - b0, 1);
+        const int u = t - b0 * NT;
+        const int nfull = (NT / kNtGroup) * kNtGroup * nb;      // tiles in whole n-tile groups
+        if (u < nfull) {
+            const int grp = u / (kNtGroup * nb), r = u - grp * (kNtGroup * nb);
+            b = b0 + r / kNtGroup;
+            nt = grp * kNtGroup + r % kNtGroup;
+        } else {
+            const int rs = NT % kNtGroup, r = u - nfull;
+            b = b0 + r / rs;
+            nt = (NT / kNtGroup) * kNtGroup + r % rs;
+        }
+        // wave-uniform by construction; the offsets come from LDS, so say so for the scalar DMA bases
+        b = __builtin_amdgcn_readfirstlane(min(max(b, 0), nblocks - 1));   // inconsistent offsets only
+        nt = __builtin_amdgcn_readfirstlane(min(max(nt, 0), NT - 1));
+        le = __builtin_amdgcn_readfirstlane(le);
     };
     // weight row (relative to the tile's first weight row) of B tile row r
     auto b_row = [&](int r) { return kGemm1 ? (r < 128 ? r : p.I - 128 + r) : r; };
@@ -205,7 +213,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes repeat lane 0's load
     const int sm_role = lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? 1 : (!kGemm1 && lane < 2 * SA_LANES + 2) ? 2 : 3;
     const int sm_row = wave * SA_LANES + (sm_role == 0 ? lane : sm_role == 2 ? lane - SA_LANES - 2 : 0);
-    const uint32_t sm_inc = sm_role == 2 ? 0u : 4u;     // bytes per K step
+    // bytes per K step: token scales are block-major (BM per K block), weight scales K-contiguous
+    const uint32_t sm_inc = sm_role == 2 ? 0u : sm_role == 1 ? 4u : (uint32_t)(BM * 4);
 
     // issue side: the next step to load, tile ij and K step ikb; the base pointers advance by one K
     // step per issue
@@ -217,9 +226,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         int b, nt, le;
         tile_of(ij, b, nt, le);
         const size_t row0 = (size_t)b * BM;
-        iA = a_base(b);
-        iW = w_base(le, nt);
-        const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (row0 + sm_row) * KB;
+        iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b)));
+        iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt)));
+        const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (size_t)b * KB * BM + sm_row;
         int blk;
         if (kGemm1) blk = lane == SA_LANES ? nt : (p.I >> 7) + nt;     // gate block, up block
         else blk = nt * 2 + (wn * WROWS) / 128;
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                         *reinterpret_cast<v4f*>(go + I + col) = acc[a + HA][t];
                     }
                 }
-                if (wn == 0 && g == 0) p.l2_sf[row * (size_t)(I >> 7) + nt] = sc;
+                if (wn == 0 && g == 0) p.l2_sf[((size_t)b * (I >> 7) + nt) * BM + tok] = sc;
             }
             lds_barrier();      // sRed is rewritten by the next tile
         } else {

@@ -33,11 +33,11 @@ struct Params {
     int* block_index;     // [max_blocks]
     int* table;           // [El][S][T_max]
     uint8_t* pool_x;      // [rows][H]
-    float* pool_sf;       // [rows][H/128]
+    float* pool_sf;       // [blocks][H/128][BM]: scale of row b*BM+i, K block kb at (b*(H/128)+kb)*BM+i
     uint32_t* pool_meta;  // [rows][3]
     uint32_t* pool_dst;   // [rows]: comb row k*S*T_max + shard*T_max + token, padding ~0
     uint8_t* l2_x;        // [rows][I]
-    float* l2_sf;         // [rows][I/128]
+    float* l2_sf;         // [blocks][I/128][BM], the same block-major order
     uint16_t* comb;       // [K][S*T_max][H]
     float* gemm1_out;     // [rows][2I] or null
     // caller tensors

@@ -98,12 +98,13 @@ typedef struct mega_moe_layout {
     uint64_t block_index;     /* int32 [max_pool_blocks]: m-block index inside its expert          */
     uint64_t table;           /* int32 [E_l][S][T_max]: t*K+k, slots >= recv[le][s] unspecified    */
     uint64_t pool_x;          /* uint8 [max_pool_blocks*BM][H] e4m3fn                              */
-    uint64_t pool_sf;         /* float [max_pool_blocks*BM][H/128]                                 */
+    uint64_t pool_sf;         /* float [max_pool_blocks][H/128][BM]: block-major, so the BM scales */
+                              /*   of one block and K block are contiguous                          */
     uint64_t pool_meta;       /* uint32 [max_pool_blocks*BM][3] = {shard, token, k}; padding = ~0  */
     uint64_t pool_dst;        /* uint32 [max_pool_blocks*BM]: comb row k*S*T_max + shard*T_max +   */
                               /*   token of the pool row (the GEMM2 scatter target); padding = ~0  */
     uint64_t l2_x;            /* uint8 [max_pool_blocks*BM][I] e4m3fn                              */
-    uint64_t l2_sf;           /* float [max_pool_blocks*BM][I/128]                                 */
+    uint64_t l2_sf;           /* float [max_pool_blocks][I/128][BM], block-major like pool_sf      */
     uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only        */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
     uint64_t total;           /* bytes needed                                                     */

@@ -61,7 +61,7 @@ class Run:
         H = sh.hidden
         cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
         px = self.region("pool_x", torch.uint8, (cap, H))[sel].cpu().numpy()
-        psf = self.region("pool_sf", torch.float32, (cap, H // 128))[sel].cpu().numpy()
+        psf = self.scales_rows("pool_sf", H // 128)[sel]
         pm = self.region("pool_meta", torch.int32, (cap, 3))[sel].cpu().numpy().view(np.uint32)
         return px, psf, pm
 
@@ -74,8 +74,14 @@ class Run:
         sh = self.shape
         cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
         q = self.region("l2_x", torch.uint8, (cap, sh.intermediate))[rows].cpu().numpy()
-        s = self.region("l2_sf", torch.float32, (cap, sh.intermediate // 128))[rows].cpu().numpy()
+        s = self.scales_rows("l2_sf", sh.intermediate // 128)[rows]
         return q, s
+
+    def scales_rows(self, name, kb):
+        """A block-major scale region ([blocks][kb][BM]) as [rows][kb]."""
+        nblk, bm = self.moe.layout["max_pool_blocks"], self.moe.block_m
+        s = self.region(name, torch.float32, (nblk, kb, bm)).cpu().numpy()
+        return np.ascontiguousarray(s.transpose(0, 2, 1)).reshape(nblk * bm, kb)
 
     def comb_row(self, k, s, t):
         sh = self.shape
