@@ -3,12 +3,14 @@
     python -m dispatch_fp8_grouped_amd.build          # or: python dispatch_fp8_grouped_amd/build.py
 
 Every source in csrc/ is compiled to an object for gfx950, then linked into
-dispatch_fp8_grouped_amd/libmegamoe.so.  Packed fp32 instructions are disabled for the device code.
+dispatch_fp8_grouped_amd/libmegamoe.so.  Packed fp32 instructions are disabled for the device code, and
+the build fails if any kernel spills registers or uses scratch memory.
 """
 from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -27,12 +29,27 @@ COMMON = [
 SOURCES = ["route.hip", "fill.hip", "gemm.hip", "combine.hip", "host.hip"]
 
 
+def _check_resources(src: str, remarks: str) -> None:
+    """Fail on any kernel that spills or uses scratch: a scratch access makes the compiler wait for
+    every outstanding vector-memory operation, which would drain the GEMM's LDS-DMA pipeline."""
+    kernel = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+            continue
+        m = re.search(r"(VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and int(m.group(2)) != 0 and not (m.group(1) == "SGPRs Spill"):
+            raise RuntimeError(f"{src}: kernel {kernel} has {m.group(1)} = {m.group(2)}")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+    _check_resources(src, res.stderr)
     return obj
 
 

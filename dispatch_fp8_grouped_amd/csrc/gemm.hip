@@ -392,7 +392,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // Promotion of MFMA k runs kLag MFMAs after it was issued (a ring of kRing products), so the
     // VALU never waits on the matrix core; the last kLag promotions of a step run at the start of
     // the next one, with the previous step's factors.
-    constexpr int kLag = 2, kRing = 4;
+    constexpr int kLag = 3, kRing = 8;
     static_assert(NMF % kRing == 0 && kLag < kRing && kLag <= NMF / 2, "promotion ring");
     v4f P[kRing];
     Frags F[2];
