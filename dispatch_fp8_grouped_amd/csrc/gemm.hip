@@ -27,8 +27,8 @@
 // tile's last ones.  Every step issues the same number of DMA instructions (past the end the last step
 // is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
 // XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
-// Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of one expert (eight
-// pool blocks x four n tiles), which share A and B through that XCD's L2.
+// Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of one expert (a few
+// n tiles of all its pool blocks), which share A and B through that XCD's L2.
 #include <type_traits>
 
 #include "mm_internal.h"
@@ -43,7 +43,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
 constexpr int kStages = 3;
-constexpr int kNtGroup = 4;       // n tiles per tile group
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // scale operands 0 select the unscaled v_mfma_f32_16x16x128_f8f6f4; format 0 = FP8 e4m3
@@ -160,10 +159,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     __syncthreads();
 
     // Tile t -> pool block, n tile and local expert.  Tiles are numbered expert by expert (expert le
-    // owns tiles [off[le]*NT, off[le+1]*NT)); inside an expert, by group of kNtGroup n tiles, then by
-    // block, then by n tile of the group.  A run of 32 consecutive tiles (one XCD's share of a round)
-    // is then 8 blocks x 4 n tiles of one expert: its A and W chunks are shared through that XCD's L2,
-    // and an expert's weights are fetched by about one XCD.
+    // owns tiles [off[le]*NT, off[le+1]*NT)), inside an expert n tile by n tile, then block by block.
+    // A run of 32 consecutive tiles (one XCD's share of a round) then covers about four n tiles of
+    // every block of one expert: the blocks' A chunks and the n tiles' W chunks are shared through
+    // that XCD's L2, each W tile is fetched by one or two XCDs and each A block about NT/4 times.
     auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
         const int t = logical + j * G;
         const int vb = t / NT;
@@ -175,16 +174,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         le = lo;
         const int b0 = sOff[lo], nb = max(sOff[lo + 1] - b0, 1);
         const int u = t - b0 * NT;
-        const int nfull = (NT / kNtGroup) * kNtGroup * nb;      // tiles in whole n-tile groups
-        if (u < nfull) {
-            const int grp = u / (kNtGroup * nb), r = u - grp * (kNtGroup * nb);
-            b = b0 + r / kNtGroup;
-            nt = grp * kNtGroup + r % kNtGroup;
-        } else {
-            const int rs = NT % kNtGroup, r = u - nfull;
-            b = b0 + r / rs;
-            nt = (NT / kNtGroup) * kNtGroup + r % rs;
-        }
+        nt = u / nb;
+        b = b0 + (u - nt * nb);
         // wave-uniform by construction; the offsets come from LDS, so say so for the scalar DMA bases
         b = __builtin_amdgcn_readfirstlane(min(max(b, 0), nblocks - 1));   // inconsistent offsets only
         nt = __builtin_amdgcn_readfirstlane(min(max(nt, 0), NT - 1));
