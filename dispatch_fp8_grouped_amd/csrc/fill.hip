@@ -11,7 +11,8 @@
 // scatter target k*S*T_max + shard*T_max + token beside them.  Rows past the expert's count are
 // padding: zero codes, zero scales, metadata and target all ones.
 //
-// One wave per pool row, 16-byte loads and stores, all loads of a row issued before its stores.
+// One wave per pool row, 16-byte loads and stores, all loads of a pass issued before its stores; the
+// kernel stays within 64 VGPRs so 8 waves per SIMD keep many rows in flight.
 #include "mm_internal.h"
 
 namespace mm {
@@ -20,7 +21,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kFillThreads = 256;
-constexpr int kUnroll = 8;   // 8 x 64 lanes x 16 B = 8 KB per batch (H <= 8192 in one batch)
+constexpr int kUnroll = 2;   // 16-byte chunks per lane per pass: the kernel fits 8 waves per SIMD
 
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
@@ -28,7 +29,7 @@ __device__ __forceinline__ int wave_min(int v) {
     return v;
 }
 
-__global__ __launch_bounds__(kFillThreads) void fill_kernel(Params p) {
+__global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     const long wave0 = (long)blockIdx.x * (kFillThreads / 64) + (threadIdx.x >> 6);
     const long nwaves = (long)gridDim.x * (kFillThreads / 64);
