@@ -5,10 +5,11 @@
 // ("Mega-MoE kernel code walkthrough: from Dispatch to WGMMA", 4.2), which makes the slot order
 // depend on timing.  Here the same counting sort ("Dispatch/Combine: blog theory vs DeepEP vs DeepGEMM
 // Mega MoE", 4.4: count, prefix sum, scatter) is done deterministically: slots of one (expert, shard)
-// follow ascending t*K+k.  Three launches:
-//   route_count  grid (chunks, S): LDS histogram of one chunk of 2048 (token, k) entries over all E
-//   route_scan   one work-group:   send[s][e], per-chunk slot bases, recv, recv_tot, pool offsets
-//                                  ("Mega-MoE notes, part 2: index table and pull", 2.4), block list
+// follow ascending t*K+k.  Four launches:
+//   route_count  grid (chunks, S): LDS histogram of one chunk of 512 (token, k) entries over all E
+//   route_scan   grid S:           send[s][e], per-chunk slot bases, recv
+//   route_pool   one work-group:   recv_tot, pool offsets ("Mega-MoE notes, part 2: index table and
+//                                  pull", 2.4), block count and block list
 //   route_table  grid (chunks, S), one wave each: stable in-wave ranking by ballot/popcount, writes
 //                table[le][s][slot] = t*K+k ("Mega-MoE notes, part 2", 1.1-1.3)
 #include "mm_internal.h"
@@ -17,8 +18,8 @@ namespace mm {
 namespace {
 
 constexpr int kCountThreads = 256;
-constexpr int kPerThread = kRouteChunk / kCountThreads;   // 8
-constexpr int kPerLane = kRouteChunk / 64;                // 32
+constexpr int kPerThread = kRouteChunk / kCountThreads;   // 2
+constexpr int kPerLane = kRouteChunk / 64;                // 8
 
 __global__ __launch_bounds__(kCountThreads) void route_count_kernel(Params p) {
     extern __shared__ int hist[];   // [E]
@@ -46,34 +47,52 @@ __global__ __launch_bounds__(kCountThreads) void route_count_kernel(Params p) {
     for (int i = tid; i < p.E; i += kCountThreads) out[i] = hist[i];
 }
 
+// One work-group per shard s: send[s][e] = sum over chunks; per local expert, the exclusive scan over
+// chunks (first slot of each chunk) and recv[le][s].
 __global__ __launch_bounds__(1024) void route_scan_kernel(Params p) {
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int* hs = p.chunk_hist + (size_t)s * p.chunks * p.E;
+    // send[s][e]: independent loads, summed in chunk order
+    for (int e = tid; e < p.E; e += 1024) {
+        const int* h = hs + e;
+        int sum = 0;
+#pragma unroll 16
+        for (int c = 0; c < p.chunks; ++c) sum += h[(size_t)c * p.E];
+        p.send[(size_t)s * p.E + e] = sum;
+    }
+    // one wave per local expert: scan over chunks, lane = chunk, 64 at a time
+    bool overflow = false;
+    for (int le = wave; le < p.El; le += 1024 / 64) {
+        const int* h = hs + p.lo + le;
+        int* base = p.chunk_base + (size_t)s * p.chunks * p.El + le;
+        int run = 0;
+        for (int c0 = 0; c0 < p.chunks; c0 += 64) {
+            const int c = c0 + lane;
+            const int v = c < p.chunks ? h[(size_t)c * p.E] : 0;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_up(incl, o);
+                if (lane >= o) incl += u;
+            }
+            if (c < p.chunks) base[(size_t)c * p.El] = run + incl - v;
+            run += __shfl(incl, 63);
+        }
+        if (lane == 0) {
+            if (run > p.T_max) { overflow = true; run = p.T_max; }
+            p.recv[(size_t)le * p.S + s] = run;
+        }
+    }
+    if (overflow) atomicOr(p.status, MEGA_MOE_STATUS_SLOT_OVERFLOW);
+}
+
+// One work-group: recv_tot, the cumulative statistics, expert-major pool offsets ("Mega-MoE notes,
+// part 2: index table and pull", 2.4), the block count and the block list.
+__global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
     __shared__ int s_tot[MEGA_MOE_MAX_LOCAL_EXPERTS];
     __shared__ int s_off[MEGA_MOE_MAX_LOCAL_EXPERTS + 1];
     const int tid = threadIdx.x;
-    // send[s][e] = sum over chunks
-    for (int i = tid; i < p.S * p.E; i += 1024) {
-        const int s = i / p.E, e = i - s * p.E;
-        const int* h = p.chunk_hist + (size_t)s * p.chunks * p.E + e;
-        int sum = 0;
-        for (int c = 0; c < p.chunks; ++c) sum += h[(size_t)c * p.E];
-        p.send[i] = sum;
-    }
-    // per (local expert, shard): exclusive scan over chunks -> first slot of each chunk; recv
-    bool overflow = false;
-    for (int i = tid; i < p.El * p.S; i += 1024) {
-        const int le = i / p.S, s = i - le * p.S;
-        const int* h = p.chunk_hist + (size_t)s * p.chunks * p.E + p.lo + le;
-        int* base = p.chunk_base + (size_t)s * p.chunks * p.El + le;
-        int run = 0;
-        for (int c = 0; c < p.chunks; ++c) {
-            base[(size_t)c * p.El] = run;
-            run += h[(size_t)c * p.E];
-        }
-        if (run > p.T_max) { overflow = true; run = p.T_max; }
-        p.recv[i] = run;   // recv[le][s]
-    }
-    if (overflow) atomicOr(p.status, MEGA_MOE_STATUS_SLOT_OVERFLOW);
-    __syncthreads();
     for (int le = tid; le < p.El; le += 1024) {
         int t = 0;
         for (int s = 0; s < p.S; ++s) t += p.recv[le * p.S + s];
@@ -106,12 +125,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(Params p) {
     }
 }
 
+// kRegRun: with at most 64 local experts the running slot of expert L lives in lane L's register (read
+// with a uniform readlane), otherwise in LDS.
+template <bool kRegRun>
 __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
-    __shared__ int run[MEGA_MOE_MAX_LOCAL_EXPERTS];
+    __shared__ int run[kRegRun ? 1 : MEGA_MOE_MAX_LOCAL_EXPERTS];
     const int c = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
     const int* base = p.chunk_base + ((size_t)s * p.chunks + c) * p.El;
-    for (int le = lane; le < p.El; le += 64) run[le] = base[le];
-    __syncthreads();
+    int run_reg = 0;
+    if (kRegRun) {
+        run_reg = lane < p.El ? base[lane] : 0;
+    } else {
+        for (int le = lane; le < p.El; le += 64) run[le] = base[le];
+        __syncthreads();
+    }
     const long n = (long)p.tps[s] * p.K;
     const long f0 = (long)c * kRouteChunk;
     const int64_t* idx = p.topk_idx + (size_t)s * p.T_max * p.K;
@@ -133,15 +160,19 @@ __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
         uint64_t pending = __ballot(le >= 0);
         while (pending) {                                 // one pass per distinct expert in the wave
             const int leader = __ffsll((unsigned long long)pending) - 1;
-            const int L = __shfl(le, leader);
+            const int L = __builtin_amdgcn_readlane(le, leader);
             const uint64_t m = __ballot(le == L);
-            const int b0 = run[L];
+            const int b0 = kRegRun ? __builtin_amdgcn_readlane(run_reg, L) : run[L];
             if (le == L) {
                 const int slot = b0 + __popcll(m & lanemask_lt());
                 if (slot < p.T_max) tab[(size_t)L * plane + slot] = f;
                 else overflow = true;
             }
-            if (lane == leader) run[L] = b0 + __popcll(m);
+            if (kRegRun) {
+                if (lane == L) run_reg = b0 + __popcll(m);
+            } else if (lane == leader) {
+                run[L] = b0 + __popcll(m);
+            }
             pending &= ~m;
         }
     }
@@ -155,10 +186,14 @@ hipError_t launch_route(const Params& p, hipStream_t stream) {
     hipLaunchKernelGGL(route_count_kernel, grid, dim3(kCountThreads), p.E * sizeof(int), stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(p.S), dim3(1024), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_table_kernel, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(route_pool_kernel, dim3(1), dim3(1024), 0, stream, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (p.El <= 64) hipLaunchKernelGGL(route_table_kernel<true>, grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL(route_table_kernel<false>, grid, dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 

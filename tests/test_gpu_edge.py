@@ -71,6 +71,19 @@ def test_random_negative_entries_and_remote_rank():
     run.close()
 
 
+def test_many_local_experts():
+    """More than 64 local experts: routing keeps the per-expert slot counters in LDS instead of lanes."""
+    print("[case] 128 local experts", flush=True)
+    sh = MoEShape("manylocal", 3, 200, 256, 128, 512, 128, 6, 64, local_rank=1, seed=25)
+    inp = make_inputs(sh, tokens_per_shard=[200, 57, 131])
+    run = Run(sh, inputs=inp)
+    n = inputs_np(run)
+    rt, _ = check_layout(run, n)
+    assert (rt.recv_tot > 0).sum() > 64
+    _whole(run, n)
+    run.close()
+
+
 def test_repeat_calls_identical_and_state_clean():
     """Two calls give identical bits; a call on other routing in between does not leak state."""
     print("[case] repeat calls", flush=True)
