@@ -41,7 +41,8 @@ NUM_STAGES = 5
 STAGE_NAMES = ("route", "fill", "gemm1", "gemm2", "combine")
 
 # Exported symbols of include/mega_moe.h
-EXPORTS = ("mega_moe_workspace_bytes", "mega_moe_init", "mega_moe_forward", "mega_moe_forward_stages",
+EXPORTS = ("mega_moe_workspace_bytes", "mega_moe_init", "mega_moe_pack_weights", "mega_moe_forward",
+           "mega_moe_forward_stages",
            "mega_moe_query_layout", "mega_moe_status", "mega_moe_set_timing", "mega_moe_stage_times",
            "mega_moe_destroy", "mega_moe_strerror")
 
@@ -85,6 +86,7 @@ def lib():
         vp, i32, u32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
         L.mega_moe_workspace_bytes.argtypes = [ctypes.POINTER(mega_moe_config), ctypes.POINTER(u64)]
         L.mega_moe_init.argtypes = [ctypes.POINTER(mega_moe_config), vp, u64, vp, ctypes.POINTER(vp)]
+        L.mega_moe_pack_weights.argtypes = [ctypes.POINTER(mega_moe_config), vp, vp, vp, vp, vp]
         fwd = [vp, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mega_moe_forward.argtypes = fwd
         L.mega_moe_forward_stages.argtypes = [vp, u32] + fwd[1:]
@@ -164,6 +166,12 @@ def mega_moe_forward_stages(h, stages: int, tokens_per_shard, x, x_sf, topk_idx,
     _check(rc, "mega_moe_forward_stages")
 
 
+def mega_moe_pack_weights(cfg: mega_moe_config, w1, w2, w1_packed, w2_packed, stream=None):
+    rc = lib().mega_moe_pack_weights(ctypes.byref(cfg), _ptr(w1), _ptr(w2), _ptr(w1_packed), _ptr(w2_packed),
+                                     _stream(stream))
+    _check(rc, "mega_moe_pack_weights")
+
+
 def mega_moe_forward(h, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y,
                      cum_recv_stats=None, stream=None):
     rc = lib().mega_moe_forward(h, _tps_array(tokens_per_shard), _ptr(x), _ptr(x_sf), _ptr(topk_idx),
@@ -241,8 +249,10 @@ class MegaMoE:
         want = [("x", x, (S, T, H), torch.uint8), ("x_sf", x_sf, (S, T, H // 128), torch.float32),
                 ("topk_idx", topk_idx, (S, T, K), torch.int64),
                 ("topk_weights", topk_weights, (S, T, K), torch.float32),
-                ("w1", w1, (El, 2 * I, H), torch.uint8), ("w1_sf", w1_sf, (El, 2 * I // 128, H // 128), torch.float32),
-                ("w2", w2, (El, H, I), torch.uint8), ("w2_sf", w2_sf, (El, H // 128, I // 128), torch.float32),
+                ("w1 (packed)", w1, self.packed_shapes()[0], torch.uint8),
+                ("w1_sf", w1_sf, (El, 2 * I // 128, H // 128), torch.float32),
+                ("w2 (packed)", w2, self.packed_shapes()[1], torch.uint8),
+                ("w2_sf", w2_sf, (El, H // 128, I // 128), torch.float32),
                 ("y", y, (S, T, H), torch.bfloat16)]
         for name, t, shape, dtype in want:
             if t is None:
@@ -250,6 +260,26 @@ class MegaMoE:
             if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"{name}: want contiguous cuda {dtype} {shape}, got {t.dtype} "
                                  f"{tuple(t.shape)} on {t.device}")
+
+    def packed_shapes(self):
+        """Shapes of the packed W1 and W2 (see mega_moe_pack_weights)."""
+        c = self.cfg
+        El, H, I = c.num_local_experts, c.hidden, c.intermediate
+        return (El, I // 128, H // 128, 256, 128), (El, H // 256, I // 128, 256, 128)
+
+    def pack_weights(self, w1, w2, stream=None):
+        """Row-major W1 [E_l,2I,H] and W2 [E_l,H,I] (uint8 e4m3fn) -> new packed tensors (w1p, w2p)."""
+        import torch
+        c = self.cfg
+        El, H, I = c.num_local_experts, c.hidden, c.intermediate
+        for name, t, shape in (("w1", w1, (El, 2 * I, H)), ("w2", w2, (El, H, I))):
+            if tuple(t.shape) != shape or t.dtype != torch.uint8 or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"{name}: want contiguous cuda uint8 {shape}, got {t.dtype} {tuple(t.shape)}")
+        s1, s2 = self.packed_shapes()
+        w1p = torch.empty(s1, dtype=torch.uint8, device=w1.device)
+        w2p = torch.empty(s2, dtype=torch.uint8, device=w2.device)
+        mega_moe_pack_weights(self.cfg, w1, w2, w1p, w2p, stream)
+        return w1p, w2p
 
     def forward(self, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y=None,
                 cum_recv_stats=None, stream=None, stages=STAGE_ALL):
@@ -264,9 +294,14 @@ class MegaMoE:
         return y
 
     def __call__(self, inputs: dict, y=None, cum_recv_stats=None, stream=None, stages=STAGE_ALL):
+        """Forward on an input dict.  The packed weights are taken from inputs["w1_packed"] /
+        inputs["w2_packed"]; when absent they are packed from inputs["w1"] / inputs["w2"] once and stored
+        there (the one-time weight transform)."""
+        if "w1_packed" not in inputs or "w2_packed" not in inputs:
+            inputs["w1_packed"], inputs["w2_packed"] = self.pack_weights(inputs["w1"], inputs["w2"], stream)
         return self.forward(inputs["tokens_per_shard"], inputs["x"], inputs["x_sf"], inputs["topk_idx"],
-                            inputs["topk_weights"], inputs["w1"], inputs["w1_sf"], inputs["w2"], inputs["w2_sf"],
-                            y, cum_recv_stats, stream, stages)
+                            inputs["topk_weights"], inputs["w1_packed"], inputs["w1_sf"], inputs["w2_packed"],
+                            inputs["w2_sf"], y, cum_recv_stats, stream, stages)
 
     def status(self, stream=None) -> int:
         return mega_moe_status(self.h, stream)

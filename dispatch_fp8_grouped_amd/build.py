@@ -26,7 +26,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-disable-promote-alloca-to-lds",
 ]
-SOURCES = ["route.hip", "fill.hip", "gemm.hip", "combine.hip", "host.hip"]
+SOURCES = ["route.hip", "fill.hip", "gemm.hip", "combine.hip", "pack.hip", "host.hip"]
 
 
 def _check_resources(src: str, remarks: str) -> None:

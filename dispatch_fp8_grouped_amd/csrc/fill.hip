@@ -6,7 +6,7 @@
 // the sources that still have rows, each such source gives L slots, and positions inside a round
 // alternate between the active sources in ascending order.  One lane per source runs the rounds with
 // wave ballots and a wave-wide minimum.  The table entry t*K+k at (le, source, slot) names the token;
-// its H-byte row, its H/128 scales and the metadata {shard, token, k} are copied
+// its H-byte row (into the tiled pool), its H/128 scales and the metadata {shard, token, k} are copied
 // ("Mega-MoE notes, part 2", 2.6; "Dispatch/Combine ... comparison", 6.2), with the row's GEMM2
 // scatter target k*S*T_max + shard*T_max + token beside them.  Rows past the expert's count are
 // padding: zero codes, zero scales, metadata and target all ones.
@@ -41,13 +41,15 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
         const int le = min(max(p.block_expert[b], 0), p.El - 1);
         const int j = p.block_index[b] * p.BM + (int)(row - (long)b * p.BM);
         const int n = p.recv_tot[le];
-        v4i* dst = reinterpret_cast<v4i*>(p.pool_x + (size_t)row * p.H);
+        // the pool is tiled: 16-byte chunk i of the row (K block i/8) at dst[(i/8)*BM*8 + i%8]
+        v4i* dst = reinterpret_cast<v4i*>(p.pool_x + (size_t)b * SF * p.BM * 128) + (row - (long)b * p.BM) * 8;
+        const int kstride = p.BM * 8;
         // scales are block-major: K block i of this row at dsf[i * BM]
         float* dsf = p.pool_sf + (size_t)b * SF * p.BM + (row - (long)b * p.BM);
         uint32_t* meta = p.pool_meta + (size_t)row * 3;
         if (j >= n) {
             const v4i z = {0, 0, 0, 0};
-            for (int i = lane; i < H16; i += 64) dst[i] = z;
+            for (int i = lane; i < H16; i += 64) dst[(i >> 3) * kstride + (i & 7)] = z;
             for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
             if (lane == 3) p.pool_dst[row] = kMetaPad;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
         const int v = slot < p.T_max ? p.table[((size_t)le * p.S + src) * p.T_max + slot] : -1;
         if (v < 0 || v >= p.tps[src] * p.K) {              // never for metadata the routing stage made
             if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
-            for (int i = lane; i < H16; i += 64) dst[i] = v4i{0, 0, 0, 0};
+            for (int i = lane; i < H16; i += 64) dst[(i >> 3) * kstride + (i & 7)] = v4i{0, 0, 0, 0};
             for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = 0.f;
             if (lane < 3) meta[lane] = kMetaPad;
             if (lane == 3) p.pool_dst[row] = kMetaPad;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int i = base + u * 64 + lane;
-                if (i < H16) dst[i] = r[u];
+                if (i < H16) dst[(i >> 3) * kstride + (i & 7)] = r[u];
             }
         }
         const float* ssf = p.x_sf + srow * SF;

@@ -181,11 +181,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         nt = __builtin_amdgcn_readfirstlane(min(max(nt, 0), NT - 1));
         le = __builtin_amdgcn_readfirstlane(le);
     };
-    // weight row (relative to the tile's first weight row) of B tile row r
-    auto b_row = [&](int r) { return kGemm1 ? (r < 128 ? r : p.I - 128 + r) : r; };
-    auto a_base = [&](int b) { return (kGemm1 ? p.pool_x : p.l2_x) + (size_t)b * BM * Kdim; };
+    // A (pool or L2 pool) and W (packed weights) are tiled: the K step kb of block b is the contiguous
+    // BM x 128 chunk at a_base(b) + kb*BM*128, that of n tile nt of expert le the 256 x 128 chunk at
+    // w_base(le, nt) + kb*256*128 (for GEMM1 its rows are the 128 gate rows, then the 128 up rows)
+    auto a_base = [&](int b) { return (kGemm1 ? p.pool_x : p.l2_x) + (size_t)b * KB * BM * 128; };
     auto w_base = [&](int le, int nt) {
-        return kGemm1 ? p.w1 + ((size_t)le * (2 * p.I) + nt * 128) * p.H : p.w2 + ((size_t)le * p.H + nt * 256) * p.I;
+        return (kGemm1 ? p.w1 : p.w2) + ((size_t)le * NT + nt) * KB * (256 * 128);
     };
 
     // per-lane DMA offsets (fixed for the whole kernel)
@@ -193,12 +194,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
         const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
-        a_off[i] = r * Kdim + c * 16;
+        a_off[i] = r * 128 + c * 16;
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
-        b_off[i] = b_row(r) * Kdim + c * 16;
+        b_off[i] = r * 128 + c * 16;
     }
     // lane role in the small DMA: token scale of row wave*SA_LANES + l, weight-block scale j, or
     // (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes repeat lane 0's load
@@ -243,8 +244,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     auto issue_advance = [&]() __attribute__((always_inline)) {
         if (ikb + 1 < KB) {
             ++ikb;
-            iA += 128;
-            iW += 128;
+            iA += BM * 128;
+            iW += 256 * 128;
             iSm += sm_inc;
         } else if (ij + 1 < my_tiles) {
             ikb = 0;
@@ -347,7 +348,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                     const int col = nt * 128 + wn * HC + a * 16 + 4 * g;
                     const uint32_t q = cvt_fp8x4(h[a][t][0] / sc, h[a][t][1] / sc, h[a][t][2] / sc,
                                                  h[a][t][3] / sc);
-                    *reinterpret_cast<uint32_t*>(p.l2_x + row * I + col) = q;
+                    // tiled L2 pool: K block nt of GEMM2 is this n tile
+                    *reinterpret_cast<uint32_t*>(p.l2_x + (((size_t)b * (I >> 7) + nt) * BM + tok) * 128 +
+                                                 (col - nt * 128)) = q;
                     if (p.gemm1_out) {
                         float* go = p.gemm1_out + row * (size_t)(2 * I);
                         *reinterpret_cast<v4f*>(go + col) = acc[a][t];

@@ -146,6 +146,23 @@ int32_t mega_moe_workspace_bytes(const mega_moe_config* cfg, uint64_t* bytes_out
     return MEGA_MOE_OK;
 }
 
+int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const void* w2, void* w1_packed,
+                              void* w2_packed, void* stream) {
+    if (!cfg || !w1 || !w2 || !w1_packed || !w2_packed) return MEGA_MOE_ERR_INVALID_ARG;
+    const int32_t rc = check_config(cfg);
+    if (rc) return rc;
+    if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1_packed) || !aligned16(w2_packed))
+        return MEGA_MOE_ERR_INVALID_ARG;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return MEGA_MOE_ERR_HIP;
+    if (mm::launch_pack(w1, w2, w1_packed, w2_packed, cfg->num_local_experts, cfg->hidden, cfg->intermediate, cus,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MEGA_MOE_ERR_HIP;
+    return MEGA_MOE_OK;
+}
+
 int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t workspace_bytes, void* stream,
                       mega_moe_handle** out) {
     if (!cfg || !out) return MEGA_MOE_ERR_INVALID_ARG;

@@ -59,6 +59,8 @@ hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_gemm1(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
+hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, int num_cus,
+                       hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

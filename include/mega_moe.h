@@ -97,13 +97,15 @@ typedef struct mega_moe_layout {
     uint64_t block_expert;    /* int32 [max_pool_blocks]: local expert of each pool block          */
     uint64_t block_index;     /* int32 [max_pool_blocks]: m-block index inside its expert          */
     uint64_t table;           /* int32 [E_l][S][T_max]: t*K+k, slots >= recv[le][s] unspecified    */
-    uint64_t pool_x;          /* uint8 [max_pool_blocks*BM][H] e4m3fn                              */
+    uint64_t pool_x;          /* uint8 [max_pool_blocks][H/128][BM][128] e4m3fn: pool row b*BM+m,  */
+                              /*   columns kb*128..+127 at ((b*(H/128) + kb)*BM + m)*128 (tiled, so */
+                              /*   one block's K step is one contiguous 16 KB chunk at BM = 128)     */
     uint64_t pool_sf;         /* float [max_pool_blocks][H/128][BM]: block-major, so the BM scales */
                               /*   of one block and K block are contiguous                          */
     uint64_t pool_meta;       /* uint32 [max_pool_blocks*BM][3] = {shard, token, k}; padding = ~0  */
     uint64_t pool_dst;        /* uint32 [max_pool_blocks*BM]: comb row k*S*T_max + shard*T_max +   */
                               /*   token of the pool row (the GEMM2 scatter target); padding = ~0  */
-    uint64_t l2_x;            /* uint8 [max_pool_blocks*BM][I] e4m3fn                              */
+    uint64_t l2_x;            /* uint8 [max_pool_blocks][I/128][BM][128] e4m3fn, tiled like pool_x */
     uint64_t l2_sf;           /* float [max_pool_blocks][I/128][BM], block-major like pool_sf      */
     uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only        */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
@@ -124,6 +126,20 @@ int32_t mega_moe_workspace_bytes(const mega_moe_config* cfg, uint64_t* bytes_out
 int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t workspace_bytes, void* stream,
                       mega_moe_handle** out /* host */);
 
+/* One-time weight transform (the pages' kernels take their weights in a transformed layout too:
+ * "DeepGEMM Mega MoE symmetric memory deep analysis", 10.2).  Copies W1 and W2 into the tiled order the
+ * grouped GEMMs stream, where one K step of one n tile is one contiguous 32 KB chunk:
+ *   w1_packed  uint8 [E_l][I/128][H/128][256][128]: chunk (le, nt, kb), row r, byte j holds
+ *              W1[le][r < 128 ? nt*128 + r : I + nt*128 + r - 128][kb*128 + j]   (128 gate rows, then
+ *              the matching 128 up rows)
+ *   w2_packed  uint8 [E_l][H/256][I/128][256][128]: chunk (le, nt, kb), row r, byte j holds
+ *              W2[le][nt*256 + r][kb*128 + j]
+ * w1 / w2 are the row-major [E_l][2I][H] / [E_l][H][I] e4m3fn tensors below; the packed buffers have the
+ * same byte counts and must not overlap them.  Asynchronous on `stream`; no handle is needed.
+ * Errors: INVALID_ARG (null or not 16-byte aligned pointer), UNSUPPORTED (config), HIP. */
+int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const void* w2, void* w1_packed,
+                              void* w2_packed, void* stream);
+
 /* The whole layer.  Shapes (S, T_max, H, I, E_l, K from the config):
  *   tokens_per_shard  host int32 [S], each in 0..T_max: valid tokens of each shard (rows t >= T_s are
  *                     neither read nor written)
@@ -131,9 +147,10 @@ int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t work
  *   x_sf              float [S][T_max][H/128], per-token per-128-column scales
  *   topk_idx          int64 [S][T_max][K], global expert ids; < 0 means "no expert"
  *   topk_weights      float [S][T_max][K]
- *   w1                uint8 [E_l][2I][H], e4m3fn; rows 0..I-1 gate, I..2I-1 up
- *   w1_sf             float [E_l][2I/128][H/128], 128x128 block scales
- *   w2                uint8 [E_l][H][I], e4m3fn
+ *   w1                W1 packed by mega_moe_pack_weights from uint8 [E_l][2I][H] e4m3fn (rows 0..I-1
+ *                     gate, I..2I-1 up)
+ *   w1_sf             float [E_l][2I/128][H/128], 128x128 block scales of the unpacked W1
+ *   w2                W2 packed by mega_moe_pack_weights from uint8 [E_l][H][I] e4m3fn
  *   w2_sf             float [E_l][H/128][I/128]
  *   y                 bf16 [S][T_max][H] output: y[s,t] = sum over k with a local expert of
  *                     w[s,t,k] * Expert(x[s,t]); a token with no local expert gets a zero row

@@ -60,7 +60,7 @@ class Run:
         sel = slice(0, P) if rows is None else rows
         H = sh.hidden
         cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
-        px = self.region("pool_x", torch.uint8, (cap, H))[sel].cpu().numpy()
+        px = self.tiled_rows("pool_x", H)[sel]
         psf = self.scales_rows("pool_sf", H // 128)[sel]
         pm = self.region("pool_meta", torch.int32, (cap, 3))[sel].cpu().numpy().view(np.uint32)
         return px, psf, pm
@@ -73,9 +73,15 @@ class Run:
     def l2_host(self, rows):
         sh = self.shape
         cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
-        q = self.region("l2_x", torch.uint8, (cap, sh.intermediate))[rows].cpu().numpy()
+        q = self.tiled_rows("l2_x", sh.intermediate)[rows]
         s = self.scales_rows("l2_sf", sh.intermediate // 128)[rows]
         return q, s
+
+    def tiled_rows(self, name, width):
+        """A tiled code region ([blocks][width/128][BM][128]) as [rows][width]."""
+        nblk, bm = self.moe.layout["max_pool_blocks"], self.moe.block_m
+        q = self.region(name, torch.uint8, (nblk, width // 128, bm, 128)).cpu().numpy()
+        return np.ascontiguousarray(q.transpose(0, 2, 1, 3)).reshape(nblk * bm, width)
 
     def scales_rows(self, name, kb):
         """A block-major scale region ([blocks][kb][BM]) as [rows][kb]."""

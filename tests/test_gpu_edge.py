@@ -146,9 +146,10 @@ def test_host_validation_on_live_handle():
     sh = SHAPES["tiny"]
     inp = on_gpu(make_inputs(sh))
     moe = mm.MegaMoE.from_shape(sh)
+    w1p, w2p = moe.pack_weights(inp["w1"], inp["w2"])
     with pytest.raises(mm.MegaMoEError) as ei:
-        moe.forward([65], inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_weights"], inp["w1"],
-                    inp["w1_sf"], inp["w2"], inp["w2_sf"])
+        moe.forward([65], inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_weights"], w1p,
+                    inp["w1_sf"], w2p, inp["w2_sf"])
     assert ei.value.code == mm.ERR_TOO_MANY_TOKENS
     with pytest.raises(mm.MegaMoEError) as ei:
         mm.mega_moe_forward_stages(moe.h, 0x20, [64], inp["x"], inp["x_sf"], inp["topk_idx"],
@@ -163,6 +164,32 @@ def test_host_validation_on_live_handle():
     with pytest.raises(mm.MegaMoEError) as ei:
         mm.mega_moe_init(moe.cfg, small)
     assert ei.value.code == mm.ERR_WORKSPACE_TOO_SMALL
+    moe.close()
+
+
+def test_pack_weights_layout():
+    """The packed weights hold every byte of W1 / W2 at the documented tiled position."""
+    print("[case] weight pack layout", flush=True)
+    sh = MoEShape("pack", 1, 8, 512, 384, 6, 3, 2, 64, seed=26)
+    inp = on_gpu(make_inputs(sh))
+    moe = mm.MegaMoE.from_shape(sh)
+    w1p, w2p = moe.pack_weights(inp["w1"], inp["w2"])
+    torch.cuda.synchronize()
+    El, H, I = sh.num_local_experts, sh.hidden, sh.intermediate
+    w1 = inp["w1"].cpu().numpy()
+    w2 = inp["w2"].cpu().numpy()
+    # W1: n tile nt stacks gate rows nt*128.. and up rows I + nt*128..; then K chunks of 128
+    rows1 = np.concatenate([np.stack([w1[:, nt * 128:(nt + 1) * 128], w1[:, I + nt * 128:I + (nt + 1) * 128]], 1)
+                            .reshape(El, 256, H) for nt in range(I // 128)], 0)      # [NT*El, 256, H]
+    rows1 = rows1.reshape(I // 128, El, 256, H).transpose(1, 0, 2, 3)
+    want1 = rows1.reshape(El, I // 128, 256, H // 128, 128).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(w1p.cpu().numpy(), want1)
+    want2 = w2.reshape(El, H // 256, 256, I // 128, 128).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(w2p.cpu().numpy(), want2)
+    # the layer on the packed weights matches the oracle
+    run = Run(sh, inputs=inp)
+    _whole(run, inputs_np(run))
+    run.close()
     moe.close()
 
 

@@ -57,11 +57,14 @@ def test_gemm2_bit_exact_on_placed_activations(shape):
     vals = torch.arange(-8, 9, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     l2 = vals[rng.integers(0, 17, (P, I))]
     cap = run.moe.layout["max_pool_blocks"] * run.moe.block_m
-    run.region("l2_x", torch.uint8, (cap, I))[:P] = torch.from_numpy(l2).cuda()
+    # the L2 pool is tiled: [blocks][I/128][BM][128]
+    nb = P // shape.block_m
+    tiled = l2.reshape(nb, shape.block_m, I // 128, 128).transpose(0, 2, 1, 3)
+    run.region("l2_x", torch.uint8, (cap * I,))[:P * I] = torch.from_numpy(np.ascontiguousarray(tiled).reshape(-1)).cuda()
     run.region("l2_sf", torch.float32, (cap, I // 128))[:P] = 2.0 ** -4
     g = run.inp_gpu
     mm.mega_moe_forward_stages(run.moe.h, mm.STAGE_GEMM2, g["tokens_per_shard"], None, None, None, None,
-                               None, None, g["w2"], g["w2_sf"], None)
+                               None, None, g["w2_packed"], g["w2_sf"], None)
     torch.cuda.synchronize()
     assert run.moe.status() == 0
     for le in range(shape.num_local_experts):
