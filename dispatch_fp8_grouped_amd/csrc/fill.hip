@@ -1,18 +1,13 @@
 // Pool fill: the receiver-side pull of routed FP8 rows into the expert-major L1 pool.
 //
-// Pool row off[le]*BM + j (j = position inside local expert le) is resolved to a source shard and slot
-// by the min-peeling round-robin ("DeepGEMM Mega MoE symmetric memory deep analysis", 7.5; "Mega-MoE
-// notes, part 2: index table and pull", 2.5): every round takes L = the smallest remaining count over
-// the sources that still have rows, each such source gives L slots, and positions inside a round
-// alternate between the active sources in ascending order.  One lane per source runs the rounds with
-// wave ballots and a wave-wide minimum.  The table entry t*K+k at (le, source, slot) names the token;
-// its H-byte row (into the tiled pool), its H/128 scales and the metadata {shard, token, k} are copied
-// ("Mega-MoE notes, part 2", 2.6; "Dispatch/Combine ... comparison", 6.2), with the row's GEMM2
-// scatter target k*S*T_max + shard*T_max + token beside them.  Rows past the expert's count are
-// padding: zero codes, zero scales, metadata and target all ones.
+// The routing stage already resolved every pool row to its source: the round-robin position of each
+// index-table entry ("Mega-MoE notes, part 2: index table and pull", 2.5) gave the row's metadata
+// {shard, token, k}, and padding rows carry all ones.  The fill copies each row's H FP8 codes into the
+// tiled pool and its H/128 scales into the block-major scale array ("Mega-MoE notes, part 2", 2.6;
+// "Dispatch/Combine ... comparison", 6.2); padding rows get zero codes and zero scales.
 //
-// One wave per pool row, 16-byte loads and stores, all loads of a pass issued before its stores; the
-// kernel stays within 64 VGPRs so 8 waves per SIMD keep many rows in flight.
+// One wave per pool row, 16-byte loads and stores.  A wave reads the metadata of its next 64 rows in
+// one vector load (lane l: row l), so each row waits only on its own data.
 #include "mm_internal.h"
 
 namespace mm {
@@ -21,91 +16,88 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kFillThreads = 256;
-constexpr int kUnroll = 2;   // 16-byte chunks per lane per pass: the kernel fits 8 waves per SIMD
+#ifndef MM_FILL_UNROLL
+#define MM_FILL_UNROLL 4
+#endif
+constexpr int kUnroll = MM_FILL_UNROLL;   // 16-byte chunks per lane per batch
 
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
-}
-
+// Lane l copies chunks l, l+64, ... of a row.  A batch issues kUnroll loads, then kUnroll stores, with
+// no branch between them: indices past the row's end are clamped to its last chunk, so those lanes
+// copy a chunk again (the same bytes to the same place).  Straight-line code keeps the compiler's
+// memory-counter waits exact; a per-lane branch around a load or store makes it wait for every
+// outstanding access, stores included, before each store.
+// kFull: H is a multiple of 1024, so every lane has the same chunk count and no index is clamped.
+template <bool kFull>
 __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
     const int lane = threadIdx.x & 63;
-    const long wave0 = (long)blockIdx.x * (kFillThreads / 64) + (threadIdx.x >> 6);
-    const long nwaves = (long)gridDim.x * (kFillThreads / 64);
-    const long rows = (long)min((int)p.status[1], p.max_blocks) * p.BM;
+    const int wave0 = __builtin_amdgcn_readfirstlane(blockIdx.x * (kFillThreads / 64) + (threadIdx.x >> 6));
+    const int nwaves = gridDim.x * (kFillThreads / 64);
+    const int rows = min((int)p.status[1], p.max_blocks) * p.BM;
     const int H16 = p.H >> 4;
     const int SF = p.H >> 7;
-    for (long row = wave0; row < rows; row += nwaves) {
-        const int b = (int)(row / p.BM);
-        const int le = min(max(p.block_expert[b], 0), p.El - 1);
-        const int j = p.block_index[b] * p.BM + (int)(row - (long)b * p.BM);
-        const int n = p.recv_tot[le];
-        // the pool is tiled: 16-byte chunk i of the row (K block i/8) at dst[(i/8)*BM*8 + i%8]
-        v4i* dst = reinterpret_cast<v4i*>(p.pool_x + (size_t)b * SF * p.BM * 128) + (row - (long)b * p.BM) * 8;
-        const int kstride = p.BM * 8;
-        // scales are block-major: K block i of this row at dsf[i * BM]
-        float* dsf = p.pool_sf + (size_t)b * SF * p.BM + (row - (long)b * p.BM);
-        uint32_t* meta = p.pool_meta + (size_t)row * 3;
-        if (j >= n) {
-            const v4i z = {0, 0, 0, 0};
-            for (int i = lane; i < H16; i += 64) dst[(i >> 3) * kstride + (i & 7)] = z;
-            for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = 0.f;
-            if (lane < 3) meta[lane] = kMetaPad;
-            if (lane == 3) p.pool_dst[row] = kMetaPad;
-            continue;
+    const int J = (H16 + 63) >> 6;            // chunks per lane
+    const uint32_t kstride16 = (uint32_t)p.BM * 128;   // bytes between K blocks of the tiled pool
+    // chunk c of a row: source byte c*16; tiled destination byte (c/8)*BM*128 + (c%8)*16
+    auto src_off = [&](int j) -> uint32_t {
+        return kFull ? (uint32_t)j * 1024 + (uint32_t)lane * 16 : (uint32_t)min(j * 64 + lane, H16 - 1) * 16;
+    };
+    auto dst_off = [&](int j) -> uint32_t {
+        if (kFull) return (uint32_t)j * 8 * kstride16 + (uint32_t)(lane >> 3) * kstride16 + (uint32_t)(lane & 7) * 16;
+        const int c = min(j * 64 + lane, H16 - 1);
+        return (uint32_t)(c >> 3) * kstride16 + (uint32_t)(c & 7) * 16;
+    };
+    // metadata of this wave's rows wave0, wave0 + nwaves, ...: lane l holds row l of each batch of 64,
+    // read back with a uniform readlane, so a row waits only on its own data
+    const int nmine = wave0 < rows ? (rows - wave0 + nwaves - 1) / nwaves : 0;
+    for (int it0 = 0; it0 < nmine; it0 += 64) {
+        uint32_t ms = kMetaPad, mt = 0;
+        if (it0 + lane < nmine) {
+            const size_t r = (size_t)wave0 + (size_t)(it0 + lane) * nwaves;
+            ms = p.pool_meta[r * 3];
+            mt = p.pool_meta[r * 3 + 1];
         }
-        // min-peeling round-robin over the sources (lane = source shard).  Every round retires at
-        // least one source, so S rounds always suffice.
-        int rem = lane < p.S ? p.recv[le * p.S + lane] : 0;
-        int jj = j, offset = 0, src = 0, slot = 0;
-        for (int round = 0; round < p.S; ++round) {
-            const bool act = rem > 0;
-            const uint64_t am = __ballot(act);
-            const int nact = __popcll(am);
-            if (nact == 0) break;
-            const int len = wave_min(act ? rem : 0x7FFFFFFF);
-            const long nround = (long)len * nact;
-            if (jj < nround) {
-                const int target = jj % nact;
-                const uint64_t sel = __ballot(act && __popcll(am & lanemask_lt()) == target);
-                src = __ffsll((unsigned long long)sel) - 1;
-                slot = offset + jj / nact;
-                break;
+        // consume the metadata here, so the compiler's wait for it is not repeated (as a wait for every
+        // outstanding store) at the top of each row
+        asm volatile("" ::"v"(ms), "v"(mt));
+        const int cnt = min(64, nmine - it0);
+        for (int it = 0; it < cnt; ++it) {
+            const int row = wave0 + (it0 + it) * nwaves;
+            const uint32_t src = __builtin_amdgcn_readlane(ms, it), tok = __builtin_amdgcn_readlane(mt, it);
+            const int b = row / p.BM, i_in = row - b * p.BM;
+            char* dbase = reinterpret_cast<char*>(p.pool_x + (size_t)b * SF * p.BM * 128 + (size_t)i_in * 128);
+            // scales are block-major: K block i of this row at dsf[i * BM]
+            float* dsf = p.pool_sf + (size_t)b * SF * p.BM + i_in;
+            const int f0 = min(lane, SF - 1), f1 = min(64 + lane, SF - 1);
+            const bool pad = src == kMetaPad;
+            if (pad || src >= (uint32_t)p.S || tok >= (uint32_t)p.T_max) {
+                // a non-padding row outside the shards never comes from the routing stage
+                if (!pad && lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
+                const v4i z = {0, 0, 0, 0};
+                for (int j = 0; j < J; ++j) *reinterpret_cast<v4i*>(dbase + dst_off(j)) = z;
+                dsf[(size_t)f0 * p.BM] = 0.f;
+                if (SF > 64) dsf[(size_t)f1 * p.BM] = 0.f;
+                continue;
             }
-            jj -= (int)nround;
-            offset += len;
-            rem -= min(rem, len);
-        }
-        const int v = slot < p.T_max ? p.table[((size_t)le * p.S + src) * p.T_max + slot] : -1;
-        if (v < 0 || v >= p.tps[src] * p.K) {              // never for metadata the routing stage made
-            if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
-            for (int i = lane; i < H16; i += 64) dst[(i >> 3) * kstride + (i & 7)] = v4i{0, 0, 0, 0};
-            for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = 0.f;
-            if (lane < 3) meta[lane] = kMetaPad;
-            if (lane == 3) p.pool_dst[row] = kMetaPad;
-            continue;
-        }
-        const int t = v / p.K, k = v - t * p.K;
-        const size_t srow = (size_t)src * p.T_max + t;
-        const v4i* sp = reinterpret_cast<const v4i*>(p.x + srow * p.H);
-        for (int base = 0; base < H16; base += 64 * kUnroll) {
-            v4i r[kUnroll];
+            const size_t srow = (size_t)src * p.T_max + tok;
+            const char* sbase = reinterpret_cast<const char*>(p.x + srow * p.H);
+            const float* ssf = p.x_sf + srow * SF;
+            float sf0 = 0.f, sf1 = 0.f;
+            for (int j0 = 0; j0 < J; j0 += kUnroll) {
+                v4i r[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int i = base + u * 64 + lane;
-                if (i < H16) r[u] = sp[i];
-            }
+                for (int u = 0; u < kUnroll; ++u)
+                    r[u] = *reinterpret_cast<const v4i*>(sbase + src_off(min(j0 + u, J - 1)));
+                if (j0 == 0) {
+                    sf0 = ssf[f0];
+                    if (SF > 64) sf1 = ssf[f1];
+                }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int i = base + u * 64 + lane;
-                if (i < H16) dst[(i >> 3) * kstride + (i & 7)] = r[u];
+                for (int u = 0; u < kUnroll; ++u)
+                    *reinterpret_cast<v4i*>(dbase + dst_off(min(j0 + u, J - 1))) = r[u];
             }
+            dsf[(size_t)f0 * p.BM] = sf0;
+            if (SF > 64) dsf[(size_t)f1 * p.BM] = sf1;
         }
-        const float* ssf = p.x_sf + srow * SF;
-        for (int i = lane; i < SF; i += 64) dsf[(size_t)i * p.BM] = ssf[i];
-        if (lane < 3) meta[lane] = lane == 0 ? (uint32_t)src : (lane == 1 ? (uint32_t)t : (uint32_t)k);
-        if (lane == 3) p.pool_dst[row] = (uint32_t)(((size_t)k * p.S + src) * p.T_max + t);
     }
 }
 
@@ -118,7 +110,8 @@ hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream) {
     const long max_grid = (long)num_cus * 8;
     if (grid > max_grid) grid = max_grid;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
+    if (p.H % 1024 == 0) hipLaunchKernelGGL(fill_kernel<true>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
+    else hipLaunchKernelGGL(fill_kernel<false>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
@@ -76,6 +77,35 @@ __device__ __forceinline__ uint32_t cvt_fp8x4(float a, float b, float c, float d
     return (uint32_t)v;
 }
 
+// Two fp32 -> two bf16 (round to nearest even) in one word, the first value in the low half.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
+// 4x4 transpose of (register i, lane row r = lane / 16): afterwards register i of row r holds what
+// register r of row i held.  permlane32_swap exchanges the upper two rows of its first operand with
+// the lower two of its second; permlane16_swap the odd rows of the first with the even rows of the
+// second.
+__device__ __forceinline__ void transpose4_rows(uint32_t (&R)[4]) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(R[0], R[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(R[1], R[3], false, false);
+    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    R[0] = s01[0];
+    R[1] = s01[1];
+    R[2] = s23[0];
+    R[3] = s23[1];
+}
+// The value of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ v4u swap_adjacent(v4u v) {
+    return v4u{swap_adjacent(v[0]), swap_adjacent(v[1]), swap_adjacent(v[2]), swap_adjacent(v[3])};
+}
+
 // LDS DMA: every lane copies 16 bytes from base + off (or 4 bytes from its own address) to LDS at
 // dst + lane * size (dst and base wave-uniform, off per lane).  Inline asm: the waits for these writes are placed by hand
 // (wait_stage_barrier); the compiler, which cannot tell the three stages apart, would otherwise drain
@@ -108,11 +138,35 @@ __device__ __forceinline__ void wait_stage_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt immediate");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// As wait_stage_barrier, allowing N1 outstanding operations when `wide` is set (wave-uniform) and N0
+// otherwise.  A wave's vector-memory counter counts down in issue order, global stores included (an
+// LDS DMA followed by younger stores is never reported done out of order), so when a tile's epilogue
+// stores were issued after the stage being waited for, those stores may stay in flight.
+template <int N0, int N1>
+__device__ __forceinline__ void wait_stage_barrier_sel(bool wide) {
+    static_assert(N0 >= 0 && N1 >= N0 && N1 < 64, "vmcnt immediate");
+    asm volatile("s_cmp_eq_u32 %0, 0\n\t"
+                 "s_cbranch_scc1 1f\n\t"
+                 "s_waitcnt vmcnt(%2) lgkmcnt(0)\n\t"
+                 "s_branch 2f\n"
+                 "1:\n\t"
+                 "s_waitcnt vmcnt(%1) lgkmcnt(0)\n"
+                 "2:\n\t"
+                 "s_barrier"
+                 :: "s"(__builtin_amdgcn_readfirstlane((int)wide)), "n"(N0), "n"(N1) : "memory", "scc");
+}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+#ifndef MM_ROT_J
+#define MM_ROT_J 2
+#endif
+#ifndef MM_ROT_N
+#define MM_ROT_N 2
+#endif
 
 // Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.
 template <int BM, int NW, bool kGemm1>
@@ -127,6 +181,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int B_INS = 32 / NW;              // 1 KB B DMA instructions per wave and step
     constexpr int SA_LANES = BM / NW;           // token rows whose scale (and GEMM2 target) a wave loads
     constexpr int DMA_PER_STEP = A_INS + B_INS + 1;
+    // global stores every wave issues in a GEMM2 tile's epilogue: two per 16-token group
+    constexpr int kEpiStores = 2 * TM;
+    // K-start rotation per block within the expert and per n tile (see the issue side below); it
+    // shortens the down GEMM and not the gate_up GEMM, whose tiles are 3.5 times longer
+    constexpr bool kRotate = !kGemm1;
+    constexpr int kRotJ = MM_ROT_J, kRotN = MM_ROT_N;
     static_assert(A_INS >= 1 && B_INS >= 1 && 2 * SA_LANES + 2 <= 64, "tile shape");
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
 
@@ -208,9 +268,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // bytes per K step: token scales are block-major (BM per K block), weight scales K-contiguous
     const uint32_t sm_inc = sm_role == 2 ? 0u : sm_role == 1 ? 4u : (uint32_t)(BM * 4);
 
-    // issue side: the next step to load, tile ij and K step ikb; the base pointers advance by one K
-    // step per issue
-    int ij = 0, ikb = 0;
+    // Issue side: the next step to load, tile ij, its ikb-th K step, K block ikc.  With kRotate a tile
+    // walks its K blocks from a start that depends on its block and n tile, wrapping around: the
+    // work-groups that share a W chunk (same n tile, different blocks) or an A chunk (same block,
+    // different n tiles) then ask L2 for it a few steps apart instead of all at once, so one of them
+    // takes the miss and the others hit.  The base pointers advance by one K block per issue.
+    int ij = 0, ikb = 0, ikc = 0;
     const uint8_t* iA;
     const uint8_t* iW;
     const uint8_t* iSm;     // per lane
@@ -218,8 +281,14 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         int b, nt, le;
         tile_of(ij, b, nt, le);
         const size_t row0 = (size_t)b * BM;
-        iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b)));
-        iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt)));
+        if constexpr (kRotate) {
+            const int jb = __builtin_amdgcn_readfirstlane(b - sOff[le]);    // block within its expert
+            int kc = kRotJ * jb + kRotN * nt;          // mod KB on the scalar unit
+            while (kc >= KB) kc -= KB;
+            ikc = kc;
+        }
+        iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b) + (size_t)ikc * BM * 128));
+        iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt) + (size_t)ikc * 256 * 128));
         const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (size_t)b * KB * BM + sm_row;
         int blk;
         if (kGemm1) blk = lane == SA_LANES ? nt : (p.I >> 7) + nt;     // gate block, up block
@@ -227,8 +296,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         const float* wsf = (kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
                                    : p.w2_sf + (size_t)le * (p.H >> 7) * KB) + (size_t)blk * KB;
         const uint32_t* dst = p.pool_dst + row0 + sm_row;
-        iSm = sm_role == 1 ? reinterpret_cast<const uint8_t*>(wsf)
-            : sm_role == 2 ? reinterpret_cast<const uint8_t*>(dst) : reinterpret_cast<const uint8_t*>(asf);
+        iSm = (sm_role == 1 ? reinterpret_cast<const uint8_t*>(wsf)
+             : sm_role == 2 ? reinterpret_cast<const uint8_t*>(dst) : reinterpret_cast<const uint8_t*>(asf)) +
+              (size_t)ikc * sm_inc;
     };
     set_issue_tile();
     // the DMA of one K step into stage buf: straight-line code, every lane active
@@ -244,9 +314,16 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     auto issue_advance = [&]() __attribute__((always_inline)) {
         if (ikb + 1 < KB) {
             ++ikb;
-            iA += BM * 128;
-            iW += 256 * 128;
-            iSm += sm_inc;
+            if (!kRotate || ++ikc < KB) {
+                iA += BM * 128;
+                iW += 256 * 128;
+                iSm += sm_inc;
+            } else {                                    // wrap to K block 0
+                ikc = 0;
+                iA -= (size_t)(KB - 1) * BM * 128;
+                iW -= (size_t)(KB - 1) * 256 * 128;
+                iSm -= (size_t)(KB - 1) * sm_inc;
+            }
         } else if (ij + 1 < my_tiles) {
             ikb = 0;
             ++ij;
@@ -307,6 +384,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
     int cj = 0, ckb = 0;      // compute side: tile and K step
+    bool epi_prev = false;    // the previous step ended a tile (its epilogue stores may be in flight)
 
     auto epilogue = [&](const Frags& f) __attribute__((always_inline)) {
         // lane holds acc[a][t][i]: weight row wr - rr + wrow(a) + 4g + i, token wm*BM/2 + 16t + rr
@@ -361,20 +439,36 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             }
             lds_barrier();      // sRed is rewritten by the next tile
         } else {
+            // The wave's output: 16-token groups t, each token 64 bf16 columns (one 128-byte line of
+            // its combine row).  After the MFMA, lane (rr, g) holds columns 16a + 4g .. +3 of token rr
+            // for a = 0..3.  A 4x4 transpose of (register a, lane row g) gives lane (rr, g) the 32
+            // contiguous bytes of subtile g; neighbour lanes rr, rr^1 then trade halves, so each store
+            // writes 16 bytes per lane and eight lanes fill one token's line: two stores per group,
+            // eight whole lines each.  Every lane stores (padding rows, target all ones, into the
+            // spare row after the K*S*T_max combine rows), so the wave issues exactly kEpiStores
+            // stores and no branch splits them.
             const uint32_t comb_rows = (uint32_t)(p.K * p.S * p.T_max);
+            const bool odd = rr & 1;
+            const size_t col0 = (size_t)nt * 256 + wn * WROWS;
+            const uint32_t byte_off = (uint32_t)g * 32 + (odd ? 16u : 0u);
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                const uint32_t d = f.dst[kGemm1 ? 0 : t];
-                if (d >= comb_rows) continue;       // padding (all ones)
-                uint16_t* dst = p.comb + (size_t)d * p.H;
+                uint32_t R[2][4];       // [h][a]: columns 16a + 4g + 2h, +1
 #pragma unroll
                 for (int a = 0; a < WN; ++a) {
-                    const int col = nt * 256 + wn * WROWS + a * 16 + 4 * g;
-                    uint2 v;
-                    v.x = (uint32_t)f32_to_bf16(acc[a][t][0]) | ((uint32_t)f32_to_bf16(acc[a][t][1]) << 16);
-                    v.y = (uint32_t)f32_to_bf16(acc[a][t][2]) | ((uint32_t)f32_to_bf16(acc[a][t][3]) << 16);
-                    *reinterpret_cast<uint2*>(dst + col) = v;
+                    R[0][a] = bf16x2(acc[a][t][0], acc[a][t][1]);
+                    R[1][a] = bf16x2(acc[a][t][2], acc[a][t][3]);
                 }
+                transpose4_rows(R[0]);
+                transpose4_rows(R[1]);
+                const v4u lo = {R[0][0], R[1][0], R[0][1], R[1][1]};    // columns 16g + 0..7
+                const v4u hi = {R[0][2], R[1][2], R[0][3], R[1][3]};    // columns 16g + 8..15
+                const v4u recv = swap_adjacent(odd ? lo : hi);
+                const uint32_t d = min(f.dst[t], comb_rows), dn = swap_adjacent(d);
+                char* even_row = reinterpret_cast<char*>(p.comb + (size_t)(odd ? dn : d) * p.H + col0);
+                char* odd_row = reinterpret_cast<char*>(p.comb + (size_t)(odd ? d : dn) * p.H + col0);
+                *reinterpret_cast<v4u*>(even_row + byte_off) = odd ? recv : lo;
+                *reinterpret_cast<v4u*>(odd_row + byte_off) = odd ? hi : recv;
             }
         }
 #pragma unroll
@@ -413,7 +507,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             if (i == 0) load_tail(fc, bufc);
             if (i == NMF / 2) {
                 __builtin_amdgcn_sched_barrier(0);
-                wait_stage_barrier<DMA_PER_STEP>();
+                // stage s+1; when step s-1 ended a tile, its epilogue stores are younger than that
+                // stage's DMA and may stay in flight (GEMM2; GEMM1's few stores are cheaper to drain
+                // than the selection)
+                if constexpr (kGemm1) wait_stage_barrier<DMA_PER_STEP>();
+                else wait_stage_barrier_sel<DMA_PER_STEP, DMA_PER_STEP + kEpiStores>(epi_prev);
                 __builtin_amdgcn_sched_barrier(0);
                 issue_dma(ic<buf>{});
                 load_head(fn, ic<(buf + 1) % kStages>{});
@@ -433,6 +531,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
             for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(acc[a][t]));
         issue_advance();
+        epi_prev = false;
         if (++ckb == KB) {
 #pragma unroll
             for (int k = NMF - kLag; k < NMF; ++k) {
@@ -444,6 +543,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
                 for (int t = 0; t < TM; ++t) fc.sc[j][t] = 0.f;
             epilogue(fc);
+            epi_prev = true;
             ckb = 0;
             ++cj;
         }

@@ -58,6 +58,10 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->flags & ~MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
+    // pool rows and combine rows (K*S*T_max) are int32 / uint32 indices in the kernels
+    if ((int64_t)c->num_shards * c->max_tokens_per_shard * c->topk + (int64_t)c->num_local_experts * 128 >=
+        (int64_t)1 << 31)
+        return MEGA_MOE_ERR_UNSUPPORTED;
     return MEGA_MOE_OK;
 }
 
@@ -99,7 +103,7 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->pool_dst = take(rows * 4);
     L->l2_x = take(rows * I);
     L->l2_sf = take(rows * (I / 128) * 4);
-    L->comb = take(K * S * T * H * 2);
+    L->comb = take((K * S * T + 1) * H * 2);     // + one spare row: GEMM2 stores padding rows there
     L->gemm1_out = (c->flags & MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) ? take(rows * 2 * I * 4) : 0;
     L->total = o;
 }

@@ -11,7 +11,8 @@
 //   route_pool   one work-group:   recv_tot, pool offsets ("Mega-MoE notes, part 2: index table and
 //                                  pull", 2.4), block count and block list
 //   route_table  grid (chunks, S), one wave each: stable in-wave ranking by ballot/popcount, writes
-//                table[le][s][slot] = t*K+k ("Mega-MoE notes, part 2", 1.1-1.3)
+//                table[le][s][slot] = t*K+k ("Mega-MoE notes, part 2", 1.1-1.3) and the entry's pool
+//                row metadata and GEMM2 scatter target (its round-robin position, 2.5), padding rows
 #include "mm_internal.h"
 
 namespace mm {
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
         p.status[1] = (uint32_t)o;
     }
     __syncthreads();
-    const int nb = s_off[p.El];
+    const int nb = min(s_off[p.El], p.max_blocks);   // never below s_off[El]: the pool holds every row
     for (int b = tid; b < nb; b += 1024) {
         int lo = 0, hi = p.El;            // last le with s_off[le] <= b: the non-empty owner of b
         while (hi - lo > 1) {
@@ -127,36 +128,91 @@ __global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
 
 // kRegRun: with at most 64 local experts the running slot of expert L lives in lane L's register (read
 // with a uniform readlane), otherwise in LDS.
+//
+// Every table entry is also placed straight into its pool row, so the fill needs no table walk.  The
+// round-robin order ("Mega-MoE notes, part 2: index table and pull", 2.5) puts slot q of shard s of
+// expert le after every slot below q of every shard, and after the shards s' < s that still hold a slot
+// at q: with c[s'] = recv[le][s'],
+//     j(s, q) = sum over s' of min(c[s'], q)  +  #{s' < s : c[s'] > q}.
+// (Round r of the min-peeling covers the slots between two consecutive distinct counts, and the shards
+// active in it are exactly those whose count exceeds the slot.)  The row gets the metadata {s, t, k} and
+// the GEMM2 scatter target k*S*T_max + s*T_max + t; the padding rows of each expert get all ones from
+// one work-group.  recv and pool_off are staged in LDS when they fit (kStageInts), else read from
+// global memory through the same generic pointer.
+constexpr int kStageInts = 4096;
+
 template <bool kRegRun>
 __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
     __shared__ int run[kRegRun ? 1 : MEGA_MOE_MAX_LOCAL_EXPERTS];
+    __shared__ int stage[kStageInts];
     const int c = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
     const int* base = p.chunk_base + ((size_t)s * p.chunks + c) * p.El;
+    const long n = (long)p.tps[s] * p.K;
+    const long f0 = (long)c * kRouteChunk;
+    const int64_t* idx = p.topk_idx + (size_t)s * p.T_max * p.K;
+    // the chunk's expert ids first, so that their loads overlap the staging below
+    int64_t e_of[kPerLane];
+#pragma unroll
+    for (int r = 0; r < kPerLane; ++r) {
+        const long f = f0 + r * 64 + lane;
+        e_of[r] = f < n ? idx[f] : -1;
+    }
+    const bool staged = p.El * p.S + p.El + 1 <= kStageInts;
+    const int* recv_v = p.recv;
+    const int* off_v = p.pool_off;
+    if (staged) {
+        // up to 8 loads per lane in flight per round (one round for the usual El*S)
+        const int nr = p.El * p.S, n_all = nr + p.El + 1;
+        for (int i0 = 0; i0 < n_all; i0 += 64 * 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 64 + lane;
+                v[u] = i < nr ? p.recv[i] : i < n_all ? p.pool_off[i - nr] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 64 + lane;
+                if (i < n_all) stage[i] = v[u];
+            }
+        }
+        recv_v = stage;
+        off_v = stage + nr;
+    }
     int run_reg = 0;
     if (kRegRun) {
         run_reg = lane < p.El ? base[lane] : 0;
     } else {
         for (int le = lane; le < p.El; le += 64) run[le] = base[le];
-        __syncthreads();
     }
-    const long n = (long)p.tps[s] * p.K;
-    const long f0 = (long)c * kRouteChunk;
-    const int64_t* idx = p.topk_idx + (size_t)s * p.T_max * p.K;
-    // load the whole chunk first so that the 32 loads are in flight together
+    if (staged || !kRegRun) __syncthreads();
+    // padding rows of the experts this work-group owns (le = its index, then every chunks*S further):
+    // metadata and scatter target all ones
+    const size_t cap_rows = (size_t)p.max_blocks * p.BM;
+    for (int le = s * p.chunks + c; le < p.El; le += p.chunks * p.S) {
+        int tot = 0;
+        for (int sp = 0; sp < p.S; ++sp) tot += recv_v[le * p.S + sp];
+        const size_t r1 = min((size_t)off_v[le + 1] * p.BM, cap_rows);
+        for (size_t r = (size_t)off_v[le] * p.BM + tot + lane; r < r1; r += 64) {
+            p.pool_meta[r * 3] = kMetaPad;
+            p.pool_meta[r * 3 + 1] = kMetaPad;
+            p.pool_meta[r * 3 + 2] = kMetaPad;
+            p.pool_dst[r] = kMetaPad;
+        }
+    }
     int le_of[kPerLane];
 #pragma unroll
-    for (int r = 0; r < kPerLane; ++r) {
-        const long f = f0 + r * 64 + lane;
-        const int64_t e = f < n ? idx[f] : -1;
-        le_of[r] = (e >= p.lo && e < p.lo + p.El) ? (int)(e - p.lo) : -1;
-    }
+    for (int r = 0; r < kPerLane; ++r)
+        le_of[r] = (e_of[r] >= p.lo && e_of[r] < p.lo + p.El) ? (int)(e_of[r] - p.lo) : -1;
     const size_t plane = (size_t)p.S * p.T_max;      // table stride between local experts
     int* tab = p.table + (size_t)s * p.T_max;
     bool overflow = false;
+    int slot_of[kPerLane];
 #pragma unroll
     for (int r = 0; r < kPerLane; ++r) {
         const int le = le_of[r];
         const int f = (int)(f0 + r * 64 + lane);
+        slot_of[r] = p.T_max;
         uint64_t pending = __ballot(le >= 0);
         while (pending) {                                 // one pass per distinct expert in the wave
             const int leader = __ffsll((unsigned long long)pending) - 1;
@@ -165,8 +221,12 @@ __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
             const int b0 = kRegRun ? __builtin_amdgcn_readlane(run_reg, L) : run[L];
             if (le == L) {
                 const int slot = b0 + __popcll(m & lanemask_lt());
-                if (slot < p.T_max) tab[(size_t)L * plane + slot] = f;
-                else overflow = true;
+                if (slot < p.T_max) {
+                    tab[(size_t)L * plane + slot] = f;
+                    slot_of[r] = slot;
+                } else {
+                    overflow = true;
+                }
             }
             if (kRegRun) {
                 if (lane == L) run_reg = b0 + __popcll(m);
@@ -176,7 +236,35 @@ __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
             pending &= ~m;
         }
     }
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kPerLane; ++r) {
+        const int le = le_of[r], q = slot_of[r];
+        if (le < 0 || q >= p.T_max) continue;
+        const int* cnt = recv_v + le * p.S;
+        int j = 0;
+        int sp = 0;
+        for (; sp + 4 <= p.S; sp += 4) {               // four independent reads at a time
+            const int c0 = cnt[sp], c1 = cnt[sp + 1], c2 = cnt[sp + 2], c3 = cnt[sp + 3];
+            j += min(c0, q) + min(c1, q) + min(c2, q) + min(c3, q);
+            j += (sp < s && c0 > q) + (sp + 1 < s && c1 > q) + (sp + 2 < s && c2 > q) + (sp + 3 < s && c3 > q);
+        }
+        for (; sp < p.S; ++sp) {
+            const int cs = cnt[sp];
+            j += min(cs, q) + (sp < s && cs > q ? 1 : 0);
+        }
+        const size_t row = (size_t)off_v[le] * p.BM + j;
+        if (row >= cap_rows) { bad = true; continue; }   // unreachable: the pool holds every routed row
+        const int f = (int)(f0 + r * 64 + lane);
+        const int t = f / p.K, k = f - t * p.K;
+        uint32_t* meta = p.pool_meta + row * 3;
+        meta[0] = (uint32_t)s;
+        meta[1] = (uint32_t)t;
+        meta[2] = (uint32_t)k;
+        p.pool_dst[row] = (uint32_t)(((size_t)k * p.S + s) * p.T_max + t);
+    }
     if (overflow) atomicOr(p.status, MEGA_MOE_STATUS_SLOT_OVERFLOW);
+    if (bad) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
 }
 
 }  // namespace

@@ -60,8 +60,10 @@ extern "C" {
 #define MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT 0x1u   /* also store GEMM1's fp32 output [pool_rows, 2I] (tests) */
 
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
-#define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, cumulative stats */
-#define MEGA_MOE_STAGE_FILL 0x2u      /* round-robin pull into the pool (needs ROUTE's outputs)       */
+#define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */
+                                      /* scatter targets, cumulative stats                              */
+#define MEGA_MOE_STAGE_FILL 0x2u      /* copy of each pool row's codes and scales (needs ROUTE's      */
+                                      /* outputs)                                                      */
 #define MEGA_MOE_STAGE_GEMM1 0x4u     /* gate_up GEMM + SwiGLU + FP8 requant into the L2 pool          */
 #define MEGA_MOE_STAGE_GEMM2 0x8u     /* down GEMM, bf16, scatter to the combine buffer                */
 #define MEGA_MOE_STAGE_COMBINE 0x10u  /* top-k weighted combine into y                                 */
@@ -107,7 +109,8 @@ typedef struct mega_moe_layout {
                               /*   token of the pool row (the GEMM2 scatter target); padding = ~0  */
     uint64_t l2_x;            /* uint8 [max_pool_blocks][I/128][BM][128] e4m3fn, tiled like pool_x */
     uint64_t l2_sf;           /* float [max_pool_blocks][I/128][BM], block-major like pool_sf      */
-    uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only        */
+    uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only, then  */
+                              /* one spare row that takes GEMM2's padding rows                   */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
     uint64_t total;           /* bytes needed                                                     */
 } mega_moe_layout;

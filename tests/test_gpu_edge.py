@@ -210,3 +210,37 @@ def test_stage_timing():
     moe(inp)
     assert mm.mega_moe_stage_times(moe.h, with_count=True)[1] == 0     # the reset cleared the count
     moe.close()
+
+
+@pytest.mark.parametrize("case", ["zipf_uneven", "many_shards"])
+def test_route_stage_places_pool_rows(case):
+    """The routing stage alone writes every pool row's metadata and scatter target (the round-robin
+    position of each table entry, padding rows all ones), over poisoned workspace contents."""
+    print(f"[case] route-only pool metadata {case}", flush=True)
+    if case == "zipf_uneven":
+        sh = MoEShape("rz", 6, 300, 256, 128, 64, 16, 6, 64, local_rank=2, routing="zipf", seed=31)
+        tps = [300, 0, 17, 299, 151, 64]
+    else:
+        sh = MoEShape("rs", 64, 40, 256, 128, 32, 8, 4, 64, local_rank=1, seed=32)
+        tps = [(7 * i) % 41 for i in range(64)]
+    inp = make_inputs(sh, tokens_per_shard=tps)
+    moe = mm.MegaMoE.from_shape(sh)
+    cap = moe.layout["max_pool_blocks"] * moe.block_m
+    moe.region("pool_meta", torch.int32, (cap, 3)).fill_(0x5A5A5A5A)
+    moe.region("pool_dst", torch.int32, (cap,)).fill_(0x5A5A5A5A)
+    g = on_gpu(inp)
+    moe(g, stages=mm.STAGE_ROUTE)
+    torch.cuda.synchronize()
+    n = to_numpy(inp)
+    rt = oracle.route(n["topk_idx"], n["tokens_per_shard"], sh.num_experts, sh.num_local_experts, sh.local_rank)
+    _, _, pm, _ = oracle.fill_pool(n["x"], n["x_sf"], rt, moe.block_m, sh.topk)
+    rows = pm.shape[0]
+    gm = moe.region("pool_meta", torch.int32, (cap, 3))[:rows].cpu().numpy().view(np.uint32)
+    gd = moe.region("pool_dst", torch.int32, (cap,))[:rows].cpu().numpy().view(np.uint32).astype(np.uint64)
+    assert np.array_equal(gm, pm), "pool metadata"
+    pad = pm[:, 0] == 0xFFFFFFFF
+    want = np.where(pad, np.uint64(0xFFFFFFFF),
+                    (pm[:, 2].astype(np.uint64) * sh.num_shards + pm[:, 0]) * sh.max_tokens_per_shard + pm[:, 1])
+    assert np.array_equal(gd, want), "pool scatter targets"
+    assert pad.any() and (~pad).any()
+    moe.close()
