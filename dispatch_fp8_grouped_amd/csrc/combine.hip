@@ -6,15 +6,18 @@
 // 9.2: per token the top-k slots with a negative index are masked, the rest are accumulated in fp32 and
 // cast to bf16).  A token with no local expert gets a zero row; rows t >= T_s are left untouched.
 //
-// One wave per token: lanes 0..K-1 read the token's expert ids and weights, a ballot gives the local
-// slots, then each lane reduces 8 bf16 (16 bytes) per slot and chunk, two chunks in flight per lane.
+// One wave per token: lanes 0..K-1 read the token's expert ids and weights and a ballot gives the
+// local slots.  Lane l owns the 16-byte chunks l, l+64, ... of the row; a batch of kBatch chunks is
+// loaded for one slot (all loads in flight together), accumulated in fp32, and after the last slot
+// converted and stored.  The code is branch-free per lane: chunk indices past the row's end are clamped
+// to its last chunk (the same bytes are read and written again), so the compiler's memory-counter waits
+// stay exact.
 #include "mm_internal.h"
 
 namespace mm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxLocal = 8;    // slots loaded together; more are handled in further passes
 
 __device__ __forceinline__ void acc8(float* acc, const uint4& v, float w) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -25,6 +28,14 @@ __device__ __forceinline__ void acc8(float* acc, const uint4& v, float w) {
     }
 }
 
+// Two fp32 -> two bf16 (round to nearest even) in one word, the first value in the low half.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
+template <int kBatch>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     const long tok = (long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -32,7 +43,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
     if (tok >= ntok) return;
     const int s = (int)(tok / p.T_max), t = (int)(tok - (long)s * p.T_max);
     if (t >= p.tps[s]) return;
-    int k_local = 0;
     float w = 0.f;
     bool is_local = false;
     if (lane < p.K) {
@@ -40,56 +50,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
         is_local = e >= p.lo && e < p.lo + p.El;
         if (is_local) w = p.topk_w[tok * p.K + lane];
     }
-    (void)k_local;
     const uint64_t mask = __ballot(is_local);
     const int H8 = p.H >> 3;                        // 16-byte chunks per row
+    const int J = (H8 + 63) >> 6;                   // chunks per lane
     const size_t plane = (size_t)ntok * p.H;        // elements per k plane of comb
     uint4* yrow = reinterpret_cast<uint4*>(p.y + (size_t)tok * p.H);
-    for (int c0 = lane; c0 < H8; c0 += 128) {
-        const int c1 = c0 + 64;
-        float a0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float a1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        uint64_t m = mask;
-        while (m) {
-            int ks[kMaxLocal];
-            int n = 0;
+    auto chunk = [&](int j) { return min(min(j, J - 1) * 64 + lane, H8 - 1); };
+    for (int j0 = 0; j0 < J; j0 += kBatch) {
+        float a[kBatch][8];
 #pragma unroll
-            for (int u = 0; u < kMaxLocal; ++u) {
-                ks[u] = 0;
-                if (m) { ks[u] = __ffsll((unsigned long long)m) - 1; m &= m - 1; n = u + 1; }
-            }
-            uint4 v0[kMaxLocal], v1[kMaxLocal];
+        for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-            for (int u = 0; u < kMaxLocal; ++u) {
-                if (u < n) {
-                    const uint4* src = reinterpret_cast<const uint4*>(p.comb + (size_t)ks[u] * plane +
-                                                                      (size_t)tok * p.H);
-                    v0[u] = src[c0];
-                    if (c1 < H8) v1[u] = src[c1];
-                }
-            }
+            for (int i = 0; i < 8; ++i) a[u][i] = 0.f;
+        for (uint64_t m = mask; m; m &= m - 1) {          // ascending k
+            const int k = __ffsll((unsigned long long)m) - 1;
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+            const uint4* src = reinterpret_cast<const uint4*>(p.comb + (size_t)k * plane + (size_t)tok * p.H);
+            uint4 v[kBatch];
 #pragma unroll
-            for (int u = 0; u < kMaxLocal; ++u) {
-                if (u < n) {
-                    const float wk = __shfl(w, ks[u]);
-                    acc8(a0, v0[u], wk);
-                    if (c1 < H8) acc8(a1, v1[u], wk);
-                }
-            }
+            for (int u = 0; u < kBatch; ++u) v[u] = src[chunk(j0 + u)];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) acc8(a[u], v[u], wk);
         }
-        uint4 o;
-        o.x = (uint32_t)f32_to_bf16(a0[0]) | ((uint32_t)f32_to_bf16(a0[1]) << 16);
-        o.y = (uint32_t)f32_to_bf16(a0[2]) | ((uint32_t)f32_to_bf16(a0[3]) << 16);
-        o.z = (uint32_t)f32_to_bf16(a0[4]) | ((uint32_t)f32_to_bf16(a0[5]) << 16);
-        o.w = (uint32_t)f32_to_bf16(a0[6]) | ((uint32_t)f32_to_bf16(a0[7]) << 16);
-        yrow[c0] = o;
-        if (c1 < H8) {
-            o.x = (uint32_t)f32_to_bf16(a1[0]) | ((uint32_t)f32_to_bf16(a1[1]) << 16);
-            o.y = (uint32_t)f32_to_bf16(a1[2]) | ((uint32_t)f32_to_bf16(a1[3]) << 16);
-            o.z = (uint32_t)f32_to_bf16(a1[4]) | ((uint32_t)f32_to_bf16(a1[5]) << 16);
-            o.w = (uint32_t)f32_to_bf16(a1[6]) | ((uint32_t)f32_to_bf16(a1[7]) << 16);
-            yrow[c1] = o;
-        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            yrow[chunk(j0 + u)] = uint4{bf16x2(a[u][0], a[u][1]), bf16x2(a[u][2], a[u][3]),
+                                        bf16x2(a[u][4], a[u][5]), bf16x2(a[u][6], a[u][7])};
     }
 }
 
@@ -98,7 +84,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
 hipError_t launch_combine(const Params& p, hipStream_t stream) {
     const long ntok = (long)p.S * p.T_max;
     const long grid = (ntok + (kThreads / 64) - 1) / (kThreads / 64);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    // a batch that divides the chunks per lane (H/512) when it can
+    const int J = ((p.H >> 3) + 63) >> 6;
+    if (J % 7 == 0) hipLaunchKernelGGL(combine_kernel<7>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    else if (J % 8 == 0) hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
