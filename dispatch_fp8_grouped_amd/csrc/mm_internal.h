@@ -8,7 +8,7 @@
 
 namespace mm {
 
-constexpr int kRouteChunk = 512;       // flat (token, k) entries per routing work-group
+constexpr int kRouteChunk = 256;       // flat (token, k) entries per routing work-group
 constexpr int kBK = 128;               // GEMM K step = one scale block
 constexpr int kBN = 256;               // GEMM weight rows per tile
 constexpr uint32_t kMetaPad = 0xFFFFFFFFu;

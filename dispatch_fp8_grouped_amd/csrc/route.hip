@@ -6,7 +6,7 @@
 // depend on timing.  Here the same counting sort ("Dispatch/Combine: blog theory vs DeepEP vs DeepGEMM
 // Mega MoE", 4.4: count, prefix sum, scatter) is done deterministically: slots of one (expert, shard)
 // follow ascending t*K+k.  Four launches:
-//   route_count  grid (chunks, S): LDS histogram of one chunk of 512 (token, k) entries over all E
+//   route_count  grid (chunks, S): LDS histogram of one chunk of 256 (token, k) entries over all E
 //   route_scan   grid S:           send[s][e], per-chunk slot bases, recv
 //   route_pool   one work-group:   recv_tot, pool offsets ("Mega-MoE notes, part 2: index table and
 //                                  pull", 2.4), block count and block list
@@ -19,8 +19,8 @@ namespace mm {
 namespace {
 
 constexpr int kCountThreads = 256;
-constexpr int kPerThread = kRouteChunk / kCountThreads;   // 2
-constexpr int kPerLane = kRouteChunk / 64;                // 8
+constexpr int kPerThread = kRouteChunk / kCountThreads;   // 1
+constexpr int kPerLane = kRouteChunk / 64;                // 4
 
 __global__ __launch_bounds__(kCountThreads) void route_count_kernel(Params p) {
     extern __shared__ int hist[];   // [E]
