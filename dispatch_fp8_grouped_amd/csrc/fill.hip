@@ -65,38 +65,52 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
             const uint32_t src = __builtin_amdgcn_readlane(ms, it), tok = __builtin_amdgcn_readlane(mt, it);
             const int b = row / p.BM, i_in = row - b * p.BM;
             char* dbase = reinterpret_cast<char*>(p.pool_x + (size_t)b * SF * p.BM * 128 + (size_t)i_in * 128);
-            // scales are block-major: K block i of this row at dsf[i * BM]
-            float* dsf = p.pool_sf + (size_t)b * SF * p.BM + i_in;
-            const int f0 = min(lane, SF - 1), f1 = min(64 + lane, SF - 1);
             const bool pad = src == kMetaPad;
             if (pad || src >= (uint32_t)p.S || tok >= (uint32_t)p.T_max) {
                 // a non-padding row outside the shards never comes from the routing stage
                 if (!pad && lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
                 const v4i z = {0, 0, 0, 0};
                 for (int j = 0; j < J; ++j) *reinterpret_cast<v4i*>(dbase + dst_off(j)) = z;
-                dsf[(size_t)f0 * p.BM] = 0.f;
-                if (SF > 64) dsf[(size_t)f1 * p.BM] = 0.f;
                 continue;
             }
             const size_t srow = (size_t)src * p.T_max + tok;
             const char* sbase = reinterpret_cast<const char*>(p.x + srow * p.H);
-            const float* ssf = p.x_sf + srow * SF;
-            float sf0 = 0.f, sf1 = 0.f;
             for (int j0 = 0; j0 < J; j0 += kUnroll) {
                 v4i r[kUnroll];
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
                     r[u] = *reinterpret_cast<const v4i*>(sbase + src_off(min(j0 + u, J - 1)));
-                if (j0 == 0) {
-                    sf0 = ssf[f0];
-                    if (SF > 64) sf1 = ssf[f1];
-                }
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
                     *reinterpret_cast<v4i*>(dbase + dst_off(min(j0 + u, J - 1))) = r[u];
             }
-            dsf[(size_t)f0 * p.BM] = sf0;
-            if (SF > 64) dsf[(size_t)f1 * p.BM] = sf1;
+        }
+    }
+    // Scales, block-major (K block k of block b's row m at pool_sf[(b*SF + k)*BM + m]): a wave takes 64
+    // consecutive pool rows, lane = row, reads up to 32 of its row's scales at once and writes each K
+    // block's 64 values as one coalesced 256-byte store (a row-per-wave store would scatter its SF
+    // values over SF lines).  Padding rows and rows the copy above rejected get zeros.
+    // When there are fewer rows than waves (decode) the groups go to the first waves that copy no rows,
+    // so the scale pass does not queue behind a row copy.
+    const int ngroups = rows >> 6;          // BM is a multiple of 64
+    const int first = rows < nwaves ? rows : 0;
+    for (int grp = (wave0 - first + nwaves) % nwaves; grp < ngroups; grp += nwaves) {
+        const int row = grp * 64 + lane;
+        const uint32_t src = p.pool_meta[(size_t)row * 3], tok = p.pool_meta[(size_t)row * 3 + 1];
+        const bool ok = src < (uint32_t)p.S && tok < (uint32_t)p.T_max;
+        const float2* ssf = reinterpret_cast<const float2*>(p.x_sf + (ok ? ((size_t)src * p.T_max + tok) * SF : 0));
+        const int b = row / p.BM, i_in = row - b * p.BM;
+        float* dsf = p.pool_sf + (size_t)b * SF * p.BM + i_in;
+        for (int k0 = 0; k0 < SF; k0 += 32) {     // SF is even (H is a multiple of 256)
+            float2 v[16];                          // up to 32 scales in flight per lane
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = ssf[min(k0 / 2 + u, SF / 2 - 1)];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int k = min(k0 + 2 * u, SF - 2);
+                dsf[(size_t)k * p.BM] = ok ? v[u].x : 0.f;
+                dsf[(size_t)(k + 1) * p.BM] = ok ? v[u].y : 0.f;
+            }
         }
     }
 }
