@@ -254,7 +254,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
         const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
-        a_off[i] = r * 128 + c * 16;
+        // the L2 pool stores a K block as four 32-byte column quarters of BM rows each
+        a_off[i] = kGemm1 ? r * 128 + c * 16 : (c >> 1) * (BM * 32) + r * 32 + (c & 1) * 16;
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
@@ -394,6 +395,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         const size_t row0 = (size_t)b * BM;
         if (kGemm1) {
             constexpr int HA = WN / 2;
+            static_assert(HA == 2 && HC == 32 && NWN == 4, "GEMM1 epilogue store layout");
             float h[HA][TM][4];
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
@@ -421,16 +423,23 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                 for (int w = 1; w < NWN; ++w) am = fmaxf(am, sRed[tok][w]);
                 const float sc = fmaxf(am, 1e-4f) / 448.0f;
                 const size_t row = row0 + tok;
+                // codes of columns 16a + 4g .. +3 of the wave's HC = 32, one dword per a
+                uint32_t q[HA];
 #pragma unroll
-                for (int a = 0; a < HA; ++a) {
-                    const int col = nt * 128 + wn * HC + a * 16 + 4 * g;
-                    const uint32_t q = cvt_fp8x4(h[a][t][0] / sc, h[a][t][1] / sc, h[a][t][2] / sc,
-                                                 h[a][t][3] / sc);
-                    // tiled L2 pool: K block nt of GEMM2 is this n tile
-                    *reinterpret_cast<uint32_t*>(p.l2_x + (((size_t)b * (I >> 7) + nt) * BM + tok) * 128 +
-                                                 (col - nt * 128)) = q;
-                    if (p.gemm1_out) {
-                        float* go = p.gemm1_out + row * (size_t)(2 * I);
+                for (int a = 0; a < HA; ++a)
+                    q[a] = cvt_fp8x4(h[a][t][0] / sc, h[a][t][1] / sc, h[a][t][2] / sc, h[a][t][3] / sc);
+                // (register a, lane row g) -> lane row g holds bytes 8g .. 8g+7 of the token's 32
+                const auto s32 = __builtin_amdgcn_permlane32_swap(q[0], q[1], false, false);
+                const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+                // L2 pool: K block nt of GEMM2 is this n tile, stored as four 32-byte column quarters of
+                // BM rows; this wave's quarter is wn, so its 16 tokens' 32 bytes are 512 contiguous bytes
+                *reinterpret_cast<uint2*>(p.l2_x + ((size_t)b * (I >> 7) + nt) * BM * 128 + (size_t)wn * BM * 32 +
+                                          (size_t)tok * 32 + g * 8) = uint2{s16[0], s16[1]};
+                if (p.gemm1_out) {
+                    float* go = p.gemm1_out + row * (size_t)(2 * I);
+#pragma unroll
+                    for (int a = 0; a < HA; ++a) {
+                        const int col = nt * 128 + wn * HC + a * 16 + 4 * g;
                         *reinterpret_cast<v4f*>(go + col) = acc[a][t];
                         *reinterpret_cast<v4f*>(go + I + col) = acc[a + HA][t];
                     }

@@ -36,7 +36,8 @@ struct Params {
     float* pool_sf;       // [blocks][H/128][BM]: scale of row b*BM+i, K block kb at (b*(H/128)+kb)*BM+i
     uint32_t* pool_meta;  // [rows][3]
     uint32_t* pool_dst;   // [rows]: comb row k*S*T_max + shard*T_max + token, padding ~0
-    uint8_t* l2_x;        // [rows][I]
+    uint8_t* l2_x;        // [blocks][I/128][4][BM][32]: row b*BM+m, columns kb*128 + 32q .. +31 at
+                          // ((b*(I/128) + kb)*4 + q)*BM*32 + m*32
     float* l2_sf;         // [blocks][I/128][BM], the same block-major order
     uint16_t* comb;       // [K][S*T_max][H]
     float* gemm1_out;     // [rows][2I] or null

@@ -107,7 +107,8 @@ typedef struct mega_moe_layout {
     uint64_t pool_meta;       /* uint32 [max_pool_blocks*BM][3] = {shard, token, k}; padding = ~0  */
     uint64_t pool_dst;        /* uint32 [max_pool_blocks*BM]: comb row k*S*T_max + shard*T_max +   */
                               /*   token of the pool row (the GEMM2 scatter target); padding = ~0  */
-    uint64_t l2_x;            /* uint8 [max_pool_blocks][I/128][BM][128] e4m3fn, tiled like pool_x */
+    uint64_t l2_x;            /* uint8 [max_pool_blocks][I/128][4][BM][32] e4m3fn: per block and K  */
+                              /* block, four 32-column quarters of BM rows                        */
     uint64_t l2_sf;           /* float [max_pool_blocks][I/128][BM], block-major like pool_sf      */
     uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only, then  */
                               /* one spare row that takes GEMM2's padding rows                   */

@@ -73,7 +73,7 @@ class Run:
     def l2_host(self, rows):
         sh = self.shape
         cap = self.moe.layout["max_pool_blocks"] * self.moe.block_m
-        q = self.tiled_rows("l2_x", sh.intermediate)[rows]
+        q = self.l2_rows(sh.intermediate)[rows]
         s = self.scales_rows("l2_sf", sh.intermediate // 128)[rows]
         return q, s
 
@@ -82,6 +82,12 @@ class Run:
         nblk, bm = self.moe.layout["max_pool_blocks"], self.moe.block_m
         q = self.region(name, torch.uint8, (nblk, width // 128, bm, 128)).cpu().numpy()
         return np.ascontiguousarray(q.transpose(0, 2, 1, 3)).reshape(nblk * bm, width)
+
+    def l2_rows(self, width):
+        """The L2 pool ([blocks][width/128][4][BM][32]) as [rows][width]."""
+        nblk, bm = self.moe.layout["max_pool_blocks"], self.moe.block_m
+        q = self.region("l2_x", torch.uint8, (nblk, width // 128, 4, bm, 32)).cpu().numpy()
+        return np.ascontiguousarray(q.transpose(0, 3, 1, 2, 4)).reshape(nblk * bm, width)
 
     def scales_rows(self, name, kb):
         """A block-major scale region ([blocks][kb][BM]) as [rows][kb]."""

@@ -57,9 +57,9 @@ def test_gemm2_bit_exact_on_placed_activations(shape):
     vals = torch.arange(-8, 9, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     l2 = vals[rng.integers(0, 17, (P, I))]
     cap = run.moe.layout["max_pool_blocks"] * run.moe.block_m
-    # the L2 pool is tiled: [blocks][I/128][BM][128]
+    # the L2 pool is tiled: [blocks][I/128][4][BM][32]
     nb = P // shape.block_m
-    tiled = l2.reshape(nb, shape.block_m, I // 128, 128).transpose(0, 2, 1, 3)
+    tiled = l2.reshape(nb, shape.block_m, I // 128, 4, 32).transpose(0, 2, 3, 1, 4)
     run.region("l2_x", torch.uint8, (cap * I,))[:P * I] = torch.from_numpy(np.ascontiguousarray(tiled).reshape(-1)).cuda()
     run.region("l2_sf", torch.float32, (cap, I // 128))[:P] = 2.0 ** -4
     g = run.inp_gpu
