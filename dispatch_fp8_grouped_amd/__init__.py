@@ -28,8 +28,10 @@ ERR_HIP = -5
 STATUS_BAD_EXPERT_ID = 0x1
 STATUS_SLOT_OVERFLOW = 0x2
 STATUS_BAD_LAYOUT = 0x4
+STATUS_TIMEOUT = 0x8
 
 FLAG_KEEP_GEMM1_OUTPUT = 0x1
+FLAG_FILL_IN_GEMM1 = 0x2
 
 STAGE_ROUTE = 0x1
 STAGE_FILL = 0x2
@@ -63,7 +65,7 @@ class mega_moe_config(ctypes.Structure):
 
 _LAYOUT_U64 = ("status", "chunk_hist", "chunk_base", "send", "recv", "recv_tot", "pool_off", "block_expert",
                "block_index", "table", "pool_x", "pool_sf", "pool_meta", "pool_dst", "l2_x", "l2_sf", "comb", "gemm1_out",
-               "total")
+               "sched", "total")
 
 
 class mega_moe_layout(ctypes.Structure):
@@ -82,6 +84,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                f"`python -m dispatch_fp8_grouped_amd.build` (hipcc, gfx950)")
+        # torch ships its own libamdhip64.so.7. Loading torch first makes the library bind to that
+        # runtime, so torch's streams and allocations are valid handles inside it. Opened the other
+        # way round, the process would hold the system runtime and torch's stream handles would fail.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, u32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
         L.mega_moe_workspace_bytes.argtypes = [ctypes.POINTER(mega_moe_config), ctypes.POINTER(u64)]

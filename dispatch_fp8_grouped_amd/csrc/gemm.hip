@@ -158,6 +158,153 @@ __device__ __forceinline__ void wait_stage_barrier_sel(bool wide) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+
+// ---------------------------------------------------------------- pool fill inside GEMM1
+// The pull of "Mega-MoE notes, part 2: index table and pull" (2.6), with that page's per-block arrival
+// count, done by GEMM1's own work-groups before their first tile.  Work is claimed in units, in pool
+// order: per block, BM/8 units of 8 rows (codes), then BM/64 units of 64 rows (scales, written
+// block-major as whole 256-byte lines).  A wave claims a unit with one atomic (the next claim is issued
+// before the copy, so its latency hides under it), copies the unit, makes its stores visible device-wide
+// (release fence) and only then counts it in its block's arrival word and in the done word.  A unit is
+// claimed only by a running wave and nothing in a unit waits, so every wait on an arrival word ends,
+// whatever order the work-groups are dispatched in and whether or not they all fit on the GPU at once.
+// On MI355X this schedule is slower than a separate fill kernel before GEMM1 (prefill layer 2.42 vs
+// 1.97 ms): every published unit costs a device-scope L2 writeback, the polls are device-scope
+// acquires, and 8 waves per CU keep fewer rows in flight than the fill kernel's 32.  It is selected by
+// MEGA_MOE_FLAG_FILL_IN_GEMM1.
+constexpr int kFillRows = 8;                   // rows per code unit
+constexpr long long kSpinTicks = 200000000;    // ~2 s of the 100 MHz constant clock
+
+template <int BM>
+struct FillUnits {
+    static constexpr int rows = BM / kFillRows, scales = BM / 64, per_block = rows + scales;
+};
+
+__device__ __forceinline__ uint32_t claim_unit(uint32_t* ctr, int lane) {
+    uint32_t u = 0;
+    if (lane == 0) u = atomicAdd(ctr, 1u);
+    return __builtin_amdgcn_readfirstlane(u);
+}
+
+// device-scope acquire load of a schedule word, one per wave
+__device__ __forceinline__ uint32_t sched_load(const uint32_t* ptr) {
+    return __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(const_cast<uint32_t*>(ptr), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Codes of pool rows row0 .. row0+7 (one block).  Lane l copies chunk columns l, l+64, ... of every
+// row, two columns of all 8 rows per batch, all loads of a batch before its stores and no branch
+// between them; chunk indices past a row's end are clamped to its last chunk (the same bytes are
+// copied twice).  Padding rows and rows naming no valid token read token 0 and store zeros.
+template <int BM>
+__device__ __forceinline__ void fill_code_unit(const Params& p, int row0, int lane) {
+    const int H16 = p.H >> 4, J = (H16 + 63) >> 6, SF = p.H >> 7;
+    const int b = row0 / BM, i0 = row0 - b * BM;
+    const char* src[kFillRows];
+    char* dst[kFillRows];
+    bool ok[kFillRows];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kFillRows; ++r) {
+        const uint32_t ms = p.pool_meta[(size_t)(row0 + r) * 3], mt = p.pool_meta[(size_t)(row0 + r) * 3 + 1];
+        ok[r] = ms < (uint32_t)p.S && mt < (uint32_t)p.T_max;
+        bad |= !ok[r] && ms != kMetaPad;
+        src[r] = reinterpret_cast<const char*>(p.x + (ok[r] ? ((size_t)ms * p.T_max + mt) * p.H : 0));
+        dst[r] = reinterpret_cast<char*>(p.pool_x + (size_t)b * SF * BM * 128 + (size_t)(i0 + r) * 128);
+    }
+    if (bad && lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
+    // two chunk columns of all 8 rows per batch: 16 loads in flight per lane
+    for (int j0 = 0; j0 < J; j0 += 2) {
+        v4i v[2][kFillRows];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = min(min(j0 + jj, J - 1) * 64 + lane, H16 - 1);
+#pragma unroll
+            for (int r = 0; r < kFillRows; ++r) v[jj][r] = *reinterpret_cast<const v4i*>(src[r] + (size_t)c * 16);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = min(min(j0 + jj, J - 1) * 64 + lane, H16 - 1);
+            const size_t off = (size_t)(c >> 3) * (BM * 128) + (c & 7) * 16;
+            const v4i z = {0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < kFillRows; ++r) *reinterpret_cast<v4i*>(dst[r] + off) = ok[r] ? v[jj][r] : z;
+        }
+    }
+}
+
+// Scales of the 64 pool rows row0 .. row0+63 (lane = row), block-major: K block k of row i of block b
+// at pool_sf[(b*SF + k)*BM + i], so each K block's 64 values are one 256-byte store.
+template <int BM>
+__device__ __forceinline__ void fill_scale_unit(const Params& p, int row0, int lane) {
+    const int SF = p.H >> 7;
+    const int row = row0 + lane;
+    const uint32_t ms = p.pool_meta[(size_t)row * 3], mt = p.pool_meta[(size_t)row * 3 + 1];
+    const bool ok = ms < (uint32_t)p.S && mt < (uint32_t)p.T_max;
+    const float2* ssf = reinterpret_cast<const float2*>(p.x_sf + (ok ? ((size_t)ms * p.T_max + mt) * SF : 0));
+    const int b = row / BM, i_in = row - b * BM;
+    float* dsf = p.pool_sf + (size_t)b * SF * BM + i_in;
+    for (int k0 = 0; k0 < SF; k0 += 32) {     // SF is even (H is a multiple of 256)
+        float2 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = ssf[min(k0 / 2 + u, SF / 2 - 1)];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int k = min(k0 + 2 * u, SF - 2);
+            dsf[(size_t)k * BM] = ok ? v[u].x : 0.f;
+            dsf[(size_t)(k + 1) * BM] = ok ? v[u].y : 0.f;
+        }
+    }
+}
+
+// Claim, copy and publish fill units until none is left.
+template <int BM>
+__device__ __forceinline__ void fill_pool(const Params& p, int nblocks, int lane) {
+    using U = FillUnits<BM>;
+    const uint32_t total = (uint32_t)nblocks * U::per_block;
+    uint32_t u = claim_unit(p.sched + kSchedClaim, lane);
+    while (u < total) {
+        const uint32_t next = claim_unit(p.sched + kSchedClaim, lane);
+        const int b = (int)(u / U::per_block), v = (int)(u % U::per_block);
+        if (v < U::rows) fill_code_unit<BM>(p, b * BM + v * kFillRows, lane);
+        else fill_scale_unit<BM>(p, b * BM + (v - U::rows) * 64, lane);
+        __threadfence();        // the unit's stores are visible device-wide before it is counted
+        if (lane == 0) {
+            atomicAdd(p.sched + kSchedArrival + b, 1u);
+            atomicAdd(p.sched + kSchedDone, 1u);
+        }
+        u = next;
+    }
+}
+
+// Bounded spin (per wave) until *word reaches `target`; every poll is a device-scope acquire, so polls
+// are spaced by a sleep.  A wait longer than kSpinTicks latches TIMEOUT and gives up: never expected,
+// it keeps a broken schedule from hanging the GPU.
+__device__ __forceinline__ void spin_until(const Params& p, const uint32_t* word, uint32_t target, int lane) {
+    if (sched_load(word) >= target) return;
+    const long long t0 = wall_clock64();
+    while (sched_load(word) < target) {
+        if (wall_clock64() - t0 > kSpinTicks) {
+            if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_TIMEOUT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(32);
+    }
+}
+
+// Every work-group takes an exit ticket after its last access to the schedule words; the last one
+// returns them to zero, so every forward starts from a clean schedule.
+__device__ __forceinline__ void sched_exit(const Params& p, int nblocks, int tid) {
+    __shared__ int sLast;
+    __syncthreads();
+    if (tid == 0) sLast = atomicAdd(p.sched + kSchedExit, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (sLast) {
+        for (int i = tid; i < nblocks; i += blockDim.x) p.sched[kSchedArrival + i] = 0;
+        if (tid < kSchedArrival) p.sched[tid] = 0;
+    }
+}
+
 template <int V>
 using ic = std::integral_constant<int, V>;
 
@@ -168,8 +315,9 @@ using ic = std::integral_constant<int, V>;
 #define MM_ROT_N 2
 #endif
 
-// Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.
-template <int BM, int NW, bool kGemm1>
+// Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.  kFill (GEMM1 only): the work-groups
+// first pull the pool rows (fill_pool) and every tile waits for its block's arrival count.
+template <int BM, int NW, bool kGemm1, bool kFill>
 __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int NWN = NW / 2;                 // compute waves along the weight (N) side
     constexpr int TM = BM / 32;                 // 16-token subtiles per wave (wave covers BM/2 tokens)
@@ -189,6 +337,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int kRotJ = MM_ROT_J, kRotN = MM_ROT_N;
     static_assert(A_INS >= 1 && B_INS >= 1 && 2 * SA_LANES + 2 <= 64, "tile shape");
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
+    static_assert(kGemm1 || !kFill, "the fill feeds GEMM1 only");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * 128];
@@ -209,7 +358,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const int ntiles = nblocks * NT;
     const int G = gridDim.x;                    // a multiple of 8
     const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    if (logical >= ntiles) return;
+    const uint32_t fill_total = (uint32_t)nblocks * FillUnits<BM>::per_block;
+    if constexpr (kFill) fill_pool<BM>(p, nblocks, lane);
+    if (logical >= ntiles) {
+        if constexpr (kFill) sched_exit(p, nblocks, tid);
+        return;
+    }
     const int my_tiles = (ntiles - 1 - logical) / G + 1;
     const int nsteps = my_tiles * KB;
 
@@ -564,7 +718,17 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     for (int j = 0; j < NSW; ++j)
 #pragma unroll
         for (int t = 0; t < TM; ++t) F[1].sc[j][t] = 0.f;
+    if constexpr (kFill) {
+        // the page's per-block arrival check: the first tile's pool block is complete before its first
+        // load
+        int b0, nt0, le0;
+        tile_of(0, b0, nt0, le0);
+        spin_until(p, p.sched + kSchedArrival + b0, FillUnits<BM>::per_block, lane);
+    }
     issue_dma(ic<0>{});
+    // every other block before anything else is loaded: the fill's last units land while the first
+    // step's operands are in flight, and the tile loop itself needs no check
+    if constexpr (kFill) spin_until(p, p.sched + kSchedDone, fill_total, lane);
     issue_advance();
     issue_dma(ic<1>{});
     issue_advance();
@@ -586,18 +750,22 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         step(ic<2>{}, ic<1>{});
     }
     wait_all_vm();      // no LDS DMA may still be landing when the work-group ends
+    if constexpr (kFill) sched_exit(p, nblocks, tid);
 }
 
-template <int BM, bool kGemm1>
+template <int BM, bool kGemm1, bool kFill = false>
 hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     int grid = (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kFill>), dim3(grid), dim3(kWaves * 64), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm1(const Params& p, int num_cus, hipStream_t stream) {
+hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
+    if (fuse_fill)
+        return p.BM == 64 ? launch<64, true, true>(p, num_cus, stream) : launch<128, true, true>(p, num_cus, stream);
     return p.BM == 64 ? launch<64, true>(p, num_cus, stream) : launch<128, true>(p, num_cus, stream);
 }
 

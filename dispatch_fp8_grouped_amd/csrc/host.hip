@@ -55,7 +55,7 @@ int32_t check_config(const mega_moe_config* c) {
         return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->topk < 1 || c->topk > MEGA_MOE_MAX_TOPK) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->block_m != 0 && c->block_m != 64 && c->block_m != 128) return MEGA_MOE_ERR_UNSUPPORTED;
-    if (c->flags & ~MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->flags & ~(MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT | MEGA_MOE_FLAG_FILL_IN_GEMM1)) return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
     // pool rows and combine rows (K*S*T_max) are int32 / uint32 indices in the kernels
@@ -105,6 +105,7 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->l2_sf = take(rows * (I / 128) * 4);
     L->comb = take((K * S * T + 1) * H * 2);     // + one spare row: GEMM2 stores padding rows there
     L->gemm1_out = (c->flags & MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) ? take(rows * 2 * I * 4) : 0;
+    L->sched = take((mm::kSchedArrival + max_blocks) * 4);
     L->total = o;
 }
 
@@ -264,6 +265,7 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
     p.l2_sf = reinterpret_cast<float*>(w + L.l2_sf);
     p.comb = reinterpret_cast<uint16_t*>(w + L.comb);
     p.gemm1_out = L.gemm1_out ? reinterpret_cast<float*>(w + L.gemm1_out) : nullptr;
+    p.sched = reinterpret_cast<uint32_t*>(w + L.sched);
     p.x = static_cast<const uint8_t*>(x);
     p.x_sf = x_sf;
     p.topk_idx = topk_idx;
@@ -280,7 +282,9 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
     if (dev != h->device && hipSetDevice(h->device) != hipSuccess) return MEGA_MOE_ERR_HIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t rc = MEGA_MOE_OK;
-    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill, g1, g2, comb};
+    // with FILL_IN_GEMM1 (and both stages selected) the fill runs inside GEMM1's launch
+    const bool fused_fill = fill && g1 && (c.flags & MEGA_MOE_FLAG_FILL_IN_GEMM1);
+    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill && !fused_fill, g1, g2, comb};
     const int set = h->next_set % kTimingSets;
     if (h->timing && h->pending[set] && fold_times(h, set) != MEGA_MOE_OK) rc = MEGA_MOE_ERR_HIP;
     uint32_t ran_mask = 0;
@@ -294,7 +298,7 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
             switch (i) {
                 case 0: e = mm::launch_route(p, st); break;
                 case 1: e = mm::launch_fill(p, h->num_cus, st); break;
-                case 2: e = mm::launch_gemm1(p, h->num_cus, st); break;
+                case 2: e = mm::launch_gemm1(p, fused_fill, h->num_cus, st); break;
                 case 3: e = mm::launch_gemm2(p, h->num_cus, st); break;
                 default: e = mm::launch_combine(p, st); break;
             }

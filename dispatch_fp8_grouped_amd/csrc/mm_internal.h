@@ -12,6 +12,11 @@ constexpr int kRouteChunk = 256;       // flat (token, k) entries per routing wo
 constexpr int kBK = 128;               // GEMM K step = one scale block
 constexpr int kBN = 256;               // GEMM weight rows per tile
 constexpr uint32_t kMetaPad = 0xFFFFFFFFu;
+// Schedule words of the fill-inside-GEMM1 launch (workspace region `sched`, zero between forwards)
+constexpr int kSchedClaim = 0;         // next fill unit to claim
+constexpr int kSchedDone = 1;          // fill units completed
+constexpr int kSchedExit = 2;          // work-groups that have finished
+constexpr int kSchedArrival = 64;      // [kSchedArrival + b]: completed fill units of pool block b
 
 // Everything a kernel needs, passed by value (kernel arguments).
 struct Params {
@@ -41,6 +46,7 @@ struct Params {
     float* l2_sf;         // [blocks][I/128][BM], the same block-major order
     uint16_t* comb;       // [K][S*T_max][H]
     float* gemm1_out;     // [rows][2I] or null
+    uint32_t* sched;      // kSched* words, then the per-block arrival counts
     // caller tensors
     const uint8_t* x;
     const float* x_sf;
@@ -57,7 +63,8 @@ struct Params {
 // Launchers (one per translation unit), all on `stream`.  Return hipSuccess or the launch error.
 hipError_t launch_route(const Params& p, hipStream_t stream);
 hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream);
-hipError_t launch_gemm1(const Params& p, int num_cus, hipStream_t stream);
+// fuse_fill: GEMM1's work-groups also pull the pool rows, and each tile waits for its block's arrival
+hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream);
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
 hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, int num_cus,

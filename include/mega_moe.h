@@ -55,15 +55,26 @@ extern "C" {
 #define MEGA_MOE_STATUS_BAD_LAYOUT 0x4u        /* a stage found workspace metadata no earlier stage wrote
                                                   (only after mega_moe_forward_stages on hand-made data);
                                                   the affected rows were skipped */
+#define MEGA_MOE_STATUS_TIMEOUT 0x8u           /* FILL_IN_GEMM1: a GEMM1 wave waited more than about 2 s
+                                                  for pool rows to arrive (never expected: every counted
+                                                  unit is claimed by a running wave); the wait was
+                                                  abandoned and the output is undefined */
 
 /* Config flags. */
 #define MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT 0x1u   /* also store GEMM1's fp32 output [pool_rows, 2I] (tests) */
+#define MEGA_MOE_FLAG_FILL_IN_GEMM1 0x2u       /* schedule of the pages ("Mega-MoE notes, part 2: index table
+                                                  and pull", 2.6): GEMM1's work-groups pull the pool rows
+                                                  themselves, counting each block's arrival, and GEMM1 waits
+                                                  on those counts instead of a kernel boundary.  Same
+                                                  results bit for bit; slower on MI355X (each published unit
+                                                  costs a device-scope L2 writeback), so off by default */
 
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
 #define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */
                                       /* scatter targets, cumulative stats                              */
 #define MEGA_MOE_STAGE_FILL 0x2u      /* copy of each pool row's codes and scales (needs ROUTE's      */
-                                      /* outputs)                                                      */
+                                      /* outputs).  With GEMM1 also selected and FILL_IN_GEMM1 set it  */
+                                      /* runs inside GEMM1's launch, timed as part of GEMM1             */
 #define MEGA_MOE_STAGE_GEMM1 0x4u     /* gate_up GEMM + SwiGLU + FP8 requant into the L2 pool          */
 #define MEGA_MOE_STAGE_GEMM2 0x8u     /* down GEMM, bf16, scatter to the combine buffer                */
 #define MEGA_MOE_STAGE_COMBINE 0x10u  /* top-k weighted combine into y                                 */
@@ -113,6 +124,9 @@ typedef struct mega_moe_layout {
     uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only, then  */
                               /* one spare row that takes GEMM2's padding rows                   */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
+    uint64_t sched;           /* uint32 [64 + max_pool_blocks]: FILL_IN_GEMM1 schedule: [0] next     */
+                              /*   fill unit to claim, [1] units done, [2] exit ticket, [64 + b]   */
+                              /*   units of pool block b done; all zero between forwards            */
     uint64_t total;           /* bytes needed                                                     */
 } mega_moe_layout;
 

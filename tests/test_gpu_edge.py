@@ -210,6 +210,13 @@ def test_stage_timing():
     moe(inp)
     assert mm.mega_moe_stage_times(moe.h, with_count=True)[1] == 0     # the reset cleared the count
     moe.close()
+    # the fill inside GEMM1's launch is timed with GEMM1
+    fused = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_FILL_IN_GEMM1)
+    mm.mega_moe_set_timing(fused.h, True)
+    fused(inp)
+    t, n = mm.mega_moe_stage_times(fused.h, with_count=True)
+    assert n == 1 and t[1] == 0 and all(t[i] > 0 for i in (0, 2, 3, 4))
+    fused.close()
 
 
 @pytest.mark.parametrize("case", ["zipf_uneven", "many_shards"])
@@ -244,3 +251,42 @@ def test_route_stage_places_pool_rows(case):
     assert np.array_equal(gd, want), "pool scatter targets"
     assert pad.any() and (~pad).any()
     moe.close()
+
+
+def _sched_words(moe):
+    n = 64 + moe.layout["max_pool_blocks"]
+    return moe.region("sched", torch.int32, (n,)).cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["bm64_ragged", "bm128_zipf"])
+def test_fill_inside_gemm1_matches_separate_fill(case):
+    """The FILL_IN_GEMM1 schedule (GEMM1's work-groups pull the pool and wait on arrival counts) gives
+    the same pool, L2 pool and output bits as the stream-ordered fill kernel, and leaves every schedule
+    word at zero."""
+    print(f"[case] fill inside GEMM1 vs separate fill {case}", flush=True)
+    if case == "bm64_ragged":
+        sh = MoEShape("fz64", 5, 333, 1024, 256, 64, 16, 6, 64, local_rank=1, seed=41)
+        tps = [333, 0, 101, 7, 250]
+    else:
+        sh = MoEShape("fz128", 4, 700, 2048, 512, 64, 16, 8, 128, local_rank=2, routing="zipf", seed=42)
+        tps = [700, 513, 1, 650]
+    inp = make_inputs(sh, tokens_per_shard=tps)
+    runs = []
+    for flags in (mm.FLAG_FILL_IN_GEMM1, 0):
+        run = Run(sh, inputs=inp, flags=flags, repeat=2)
+        assert run.status == 0
+        assert not _sched_words(run.moe).any(), "schedule words left non-zero"
+        runs.append(run)
+    a, b = runs
+    n = inputs_np(a)
+    check_layout(a, n)
+    nb = int(a.region("status", torch.int32, (2,))[1].item())
+    rows = slice(0, nb * a.moe.block_m)
+    qa, sa = a.l2_host(rows)
+    qb, sb = b.l2_host(rows)
+    assert np.array_equal(qa, qb) and np.array_equal(sa.view(np.uint32), sb.view(np.uint32)), "L2 pool"
+    for ya, yb in zip(a.ys, b.ys):
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16)), "output bits"
+    _whole(a, n)
+    for r in runs:
+        r.close()
