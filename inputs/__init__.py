@@ -9,8 +9,9 @@ layer FP8 activations and block-scaled FP8 weights.
 Input recipe (the workload descriptions the layer is quoted on):
   * x ~ N(0, 1) of shape [S, T, H], quantised per token and per 128 columns:
     scale = amax / 448, codes = e4m3fn(x / scale).
-  * W1 ~ N(0, 0.02^2) of shape [E_l, 2I, H] (rows 0..I-1 gate, I..2I-1 up) and
-    W2 ~ N(0, 0.02^2) of shape [E_l, H, I], quantised per 128x128 block the same way.
+  * W1 ~ N(0, 0.02^2) of shape [E_l + n_shared, 2I, H] (rows 0..I-1 gate, I..2I-1 up) and
+    W2 ~ N(0, 0.02^2) of shape [E_l + n_shared, H, I], quantised per 128x128 block the same
+    way; with a shared expert (n_shared = 1) its weights are the last expert.
   * topk_idx: K distinct experts per token.  "uniform": a uniformly random K-subset.
     "zipf": expert at rank j of a seeded permutation has weight j^-alpha and K experts are
     drawn without replacement (Gumbel top-k, i.e. successive draws proportional to weight).
@@ -47,6 +48,7 @@ class MoEShape:
     block_m: int               # BLOCK_M of the expert pool
     local_rank: int = 0
     routing: str = "uniform"   # "uniform" | "zipf"
+    num_shared_experts: int = 0  # 0 or 1: a shared expert on shard local_rank's own tokens
     zipf_alpha: float = 1.2
     seed: int = 0
 
@@ -108,15 +110,16 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
     """Draw one seeded input set.  Returns a dict of tensors on ``device``:
 
     x [S,T,H] u8 (e4m3fn codes), x_sf [S,T,H/128] f32, topk_idx [S,T,K] i64,
-    topk_weights [S,T,K] f32, w1 [E_l,2I,H] u8, w1_sf [E_l,2I/128,H/128] f32,
-    w2 [E_l,H,I] u8, w2_sf [E_l,H/128,I/128] f32, and tokens_per_shard (list of int).
+    topk_weights [S,T,K] f32, w1 [E_w,2I,H] u8, w1_sf [E_w,2I/128,H/128] f32,
+    w2 [E_w,H,I] u8, w2_sf [E_w,H/128,I/128] f32 (E_w = E_l + num_shared_experts), and
+    tokens_per_shard (list of int).
 
     integer_codes=True draws every FP8 code from the integers -8..8 and every scale as
     one shared power of two (2^-4 for activations, 2^-6 for weights), so that every
     product and every partial sum of the GEMMs is exact in fp32.
     """
     S, T, H, I = shape.num_shards, shape.max_tokens_per_shard, shape.hidden, shape.intermediate
-    El, K = shape.num_local_experts, shape.topk
+    El, K = shape.num_local_experts + shape.num_shared_experts, shape.topk
     if H % 128 or I % 128:
         raise ValueError("hidden and intermediate must be multiples of 128")
     gen = torch.Generator(device=device)

@@ -149,7 +149,8 @@ def rr_position(counts: Sequence[int], s: int, q: int) -> int:
 
 
 # ----------------------------------------------------------------------------- pool fill
-def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, topk: int):
+def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, topk: int,
+              shared_shard: Optional[int] = None, shared_tokens: int = 0):
     """The expert-major L1 pool: rows, per-128 scales and source metadata.
 
     "Mega-MoE notes, part 2", 2.6 and "DeepGEMM Mega MoE symmetric memory deep analysis",
@@ -158,11 +159,20 @@ def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, to
     {rank, token, topk} ("Dispatch/Combine ... comparison", 6.2).  Rows past recv_tot in
     an expert's last block are padding: zero codes, zero scales, metadata all ones (the
     pages skip those rows and leave their content open; zeros are the reading taken here).
+
+    shared_shard: with a shared expert, one more segment follows the routed experts: the
+    shared expert reads this rank's own input tokens, not pulled ones ("DeepGEMM Mega MoE
+    symmetric memory deep analysis", 4.1: the shared expert's L1 tokens reuse the input
+    buffer), so its rows are tokens 0..shared_tokens-1 of shard `shared_shard` in order,
+    with top-k slot K (the extra combine slot, 8.2), padded to BM like every expert.  The
+    returned offsets then have E_l+2 entries, the last one ending the shared segment.
     """
     El = rt.recv.shape[0]
     H = x.shape[2]
     off = pool_offsets(rt.recv_tot, block_m)
-    P = int(off[El]) * block_m
+    if shared_shard is not None:
+        off = np.append(off, off[-1] + (int(shared_tokens) + block_m - 1) // block_m)
+    P = int(off[-1]) * block_m
     pool_x = np.zeros((P, H), dtype=np.uint8)
     pool_sf = np.zeros((P, H // 128), dtype=np.float32)
     pool_meta = np.full((P, 3), META_PAD, dtype=np.uint32)
@@ -181,6 +191,14 @@ def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, to
         pool_meta[rows, 0] = s
         pool_meta[rows, 1] = t
         pool_meta[rows, 2] = k
+    if shared_shard is not None and shared_tokens > 0:
+        t = np.arange(int(shared_tokens), dtype=np.int64)
+        rows = int(off[El]) * block_m + t
+        pool_x[rows] = x[shared_shard, t]
+        pool_sf[rows] = x_sf[shared_shard, t]
+        pool_meta[rows, 0] = shared_shard
+        pool_meta[rows, 1] = t
+        pool_meta[rows, 2] = topk
     return pool_x, pool_sf, pool_meta, off
 
 
@@ -270,7 +288,7 @@ def dequant_rows_gran(codes, sf, gran):
 # ----------------------------------------------------------------------------- full layer
 def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, local_rank: int,
             block_m: int, gran: int = 128, experts: Optional[Sequence[int]] = None,
-            keep_rows: bool = False) -> Dict[str, object]:
+            keep_rows: bool = False, num_shared_experts: int = 0) -> Dict[str, object]:
     """The whole layer on numpy inputs (the dict made by inputs.make_inputs + to_numpy).
 
     Steps in the pages' order: counts and table, pool layout, round-robin pull, GEMM1,
@@ -283,6 +301,12 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
 
     experts: restrict the FFN to these local experts (the others contribute nothing); used
     to time a bounded sample.  keep_rows: also return per-pool-row outputs and l2 parts.
+
+    num_shared_experts = 1: the shared expert (weights at index E_l of w1/w2) runs on every
+    valid token of this rank's own shard (shard local_rank), and its bf16 output is added
+    with weight 1 after the routed slots: the pages' combine walks the top-k slots and then
+    the extra shared slot K, and the shared expert's epilogue applies no routing weight
+    ("DeepGEMM Mega MoE symmetric memory deep analysis", 8.1-8.2 and 9.2).
     """
     x, x_sf = inp["x"], inp["x_sf"]
     idx, w = inp["topk_idx"], inp["topk_weights"]
@@ -291,7 +315,10 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
     H = x.shape[2]
     I = inp["w2"].shape[2]
     rt = route(idx, tps, num_experts, num_local_experts, local_rank)
-    pool_x, pool_sf, pool_meta, off = fill_pool(x, x_sf, rt, block_m, K)
+    shared = num_shared_experts > 0
+    pool_x, pool_sf, pool_meta, off = fill_pool(x, x_sf, rt, block_m, K,
+                                                shared_shard=local_rank if shared else None,
+                                                shared_tokens=int(tps[local_rank]) if shared else 0)
     y = np.zeros((S, T_max, H), dtype=np.float64)
     rows_out = {}
     parts_out = {}
@@ -311,6 +338,15 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
         if keep_rows:
             rows_out[le] = o
             parts_out[le] = parts
+    if shared and int(tps[local_rank]) > 0:
+        El, n = num_local_experts, int(tps[local_rank])
+        rows = slice(int(off[El]) * block_m, int(off[El]) * block_m + n)
+        o, parts = expert_ffn_rows(pool_x[rows], pool_sf[rows], inp["w1"][El], inp["w1_sf"][El],
+                                   inp["w2"][El], inp["w2_sf"][El], I, gran, return_parts=True)
+        y[local_rank, :n] += o
+        if keep_rows:
+            rows_out[El] = o
+            parts_out[El] = parts
     y = bf16_round(y)
     for s in range(S):
         y[s, int(tps[s]):] = np.nan
@@ -322,11 +358,13 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
 
 
 def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
-                 local_rank: int, gran: int = 128, cache: Optional[dict] = None) -> np.ndarray:
+                 local_rank: int, gran: int = 128, cache: Optional[dict] = None,
+                 num_shared_experts: int = 0) -> np.ndarray:
     """y[s,t] evaluated on its own: no counts, no table, no pool.
 
     out(T) = sum over the token's local experts of w_k * Expert_k(T) ("Dispatch/Combine ...
-    comparison", section 1), with each Expert_k the same FFN steps as the pooled path.
+    comparison", section 1), with each Expert_k the same FFN steps as the pooled path,
+    plus, with a shared expert, Shared(T) with weight 1 for the tokens of shard local_rank.
     Returns a bf16-rounded float64 row of length H.
     """
     K = inp["topk_idx"].shape[2]
@@ -335,11 +373,14 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
     a_codes = inp["x"][s, t][None, :]
     a_sf = inp["x_sf"][s, t][None, :]
     acc = np.zeros(inp["x"].shape[2], dtype=np.float64)
+    slots = []
     for k in range(K):
         e = int(inp["topk_idx"][s, t, k])
-        if e < lo or e >= lo + num_local_experts:
-            continue
-        le = e - lo
+        if lo <= e < lo + num_local_experts:
+            slots.append((e - lo, float(inp["topk_weights"][s, t, k])))
+    if num_shared_experts > 0 and s == local_rank:
+        slots.append((num_local_experts, 1.0))
+    for le, wk in slots:
         if cache is None:
             o = expert_ffn_rows(a_codes, a_sf, inp["w1"][le], inp["w1_sf"][le], inp["w2"][le],
                                 inp["w2_sf"][le], I, gran)[0]
@@ -348,5 +389,5 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
                 cache[le] = (dequant_blocks(inp["w1"][le], inp["w1_sf"][le]),
                              dequant_blocks(inp["w2"][le], inp["w2_sf"][le]))
             o = ffn_dequantised(dequant_rows(a_codes, a_sf), cache[le][0], cache[le][1], I, gran)[0]
-        acc += float(inp["topk_weights"][s, t, k]) * o
+        acc += wk * o
     return bf16_round(acc)

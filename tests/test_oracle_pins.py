@@ -393,3 +393,69 @@ def test_tokens_beyond_valid_and_no_local_expert():
     assert np.all(out["y"][0, 0] == 0)
     assert np.all(np.isnan(out["y"][1, 5:]))
     assert not np.any(np.isnan(out["y"][1, :5]))
+
+
+# ----------------------------------------------------------------------------- shared expert
+def test_shared_expert_textbook():
+    """One routed expert with weight w plus the shared expert on the rank's own shard:
+    y = bf16(w * bf16(E0(x)) + bf16(Shared(x))), each FFN through torch routines only; tokens of
+    the other shard get no shared contribution."""
+    sh = MoEShape("t", 2, 24, 256, 128, 2, 1, 1, 64, local_rank=1, num_shared_experts=1, seed=5)
+    inp = to_numpy(make_inputs(sh))
+    assert inp["w1"].shape[0] == 2           # routed expert 0, shared expert at index E_l = 1
+    inp["topk_idx"][:] = 1                   # global expert 1 = local expert 0 of rank 1
+    inp["topk_weights"][:] = 0.625
+    inp["tokens_per_shard"] = [24, 17]
+    out = oracle.forward(inp, 2, 1, 1, 64, num_shared_experts=1)
+    bf = lambda t: t.to(torch.float32).to(torch.bfloat16).to(torch.float64)  # noqa: E731
+    for s in (0, 1):
+        n = inp["tokens_per_shard"][s]
+        e0, _ = _torch_textbook(inp["x"][s, :n], inp["x_sf"][s, :n], inp["w1"][0], inp["w1_sf"][0],
+                                inp["w2"][0], inp["w2_sf"][0], 128)
+        want = 0.625 * bf(e0)
+        if s == 1:
+            sx, _ = _torch_textbook(inp["x"][s, :n], inp["x_sf"][s, :n], inp["w1"][1], inp["w1_sf"][1],
+                                    inp["w2"][1], inp["w2_sf"][1], 128)
+            want = want + bf(sx)
+        want = bf(want).numpy()
+        assert np.all(np.abs(out["y"][s, :n] - want) <= np.abs(want) * 2.0 ** -7 + 1e-30), s
+    # the shared segment follows the routed one: own shard's 17 tokens in order, slot K = 1
+    off = out["off"]
+    assert len(off) == 3 and off[2] - off[1] == 1      # E_l + 2 entries; ceil(17 / 64) blocks
+    seg = out["pool_meta"][off[1] * 64: off[1] * 64 + 64]
+    assert np.array_equal(seg[:17, 0], np.full(17, 1)) and np.array_equal(seg[:17, 1], np.arange(17))
+    assert np.array_equal(seg[:17, 2], np.full(17, 1)) and np.all(seg[17:] == 0xFFFFFFFF)
+    assert np.array_equal(out["pool_x"][off[1] * 64: off[1] * 64 + 17], inp["x"][1, :17])
+
+
+def test_shared_expert_zero_weights_reduce_to_routed_only():
+    """A shared expert with all-zero weight codes contributes exactly zero (silu(0) * 0 = 0, requant
+    of a zero row gives zero codes), so the output equals the layer without one, bit for bit."""
+    sh = MoEShape("t", 3, 40, 256, 256, 16, 4, 2, 64, local_rank=2, num_shared_experts=1, seed=6)
+    inp = to_numpy(make_inputs(sh))
+    inp["tokens_per_shard"] = [40, 13, 29]
+    inp["w1"][4] = 0
+    inp["w2"][4] = 0
+    with_sh = oracle.forward(inp, 16, 4, 2, 64, num_shared_experts=1)
+    plain = dict(inp)
+    for k in ("w1", "w1_sf", "w2", "w2_sf"):
+        plain[k] = inp[k][:4]
+    without = oracle.forward(plain, 16, 4, 2, 64)
+    assert np.array_equal(with_sh["y"], without["y"], equal_nan=True)
+
+
+def test_shared_expert_brute_force_pooled_equals_direct():
+    """Every routing of a tiny shape with a shared expert: pooled path == direct per-token path."""
+    K = 2
+    choices = [(a, b) for a in (-1, 0, 1) for b in (-1, 0, 1) if a < 0 or b < 0 or a != b]
+    sh = MoEShape("b", 2, 2, 128, 128, 2, 2, K, 64, local_rank=0, num_shared_experts=1, seed=7)
+    base = to_numpy(make_inputs(sh))
+    cache = {}
+    for combo in itertools.product(choices, repeat=4):
+        inp = dict(base)
+        inp["topk_idx"] = np.array(combo, dtype=np.int64).reshape(2, 2, K)
+        out = oracle.forward(inp, 2, 2, 0, 64, num_shared_experts=1)
+        for s in range(2):
+            for t in range(2):
+                d = oracle.direct_token(inp, s, t, 2, 0, cache=cache, num_shared_experts=1)
+                assert np.allclose(out["y"][s, t], d, rtol=2.0 ** -7, atol=1e-30), (combo, s, t)
