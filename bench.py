@@ -34,13 +34,14 @@ WORKLOAD_TEXT = {
 }
 
 
-def algorithmic(shape, R, N):
-    """Algorithmic work per forward (valid routed rows only, no padding)."""
+def algorithmic(shape, R, N, shared_rows=0):
+    """Algorithmic work per forward (valid routed rows only, no padding; the GEMMs also count the shared
+    expert's rows when there is one)."""
     H, I, K = shape.hidden, shape.intermediate, shape.topk
-    El = shape.num_local_experts
+    El = shape.num_local_experts + shape.num_shared_experts
     return dict(
-        gemm1_flop=4.0 * R * H * I,
-        gemm2_flop=2.0 * R * I * H,
+        gemm1_flop=4.0 * (R + shared_rows) * H * I,
+        gemm2_flop=2.0 * (R + shared_rows) * I * H,
         # route: read every (token, k) expert id, write one table entry per routed pair
         route_bytes=N * K * 8 + R * 4,
         # fill: read the row and its scales, write them and 12 B of metadata, read the table entry
@@ -92,6 +93,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-experts", type=int, default=0, choices=(0, 1),
+                    help="add a shared expert on the own shard's tokens (pool segment + combine slot K)")
     ap.add_argument("--fill-in-gemm1", action="store_true",
                     help="pull the pool rows inside GEMM1's launch, GEMM1 waiting on per-block arrival counts "
                          "(default: the fill is its own kernel, stream-ordered before GEMM1)")
@@ -121,6 +124,8 @@ def main():
     from inputs import SHAPES, make_inputs
 
     shape = SHAPES[args.workload]
+    if args.shared_experts:
+        shape = shape.replace(num_shared_experts=args.shared_experts)
     torch.cuda.set_device(0)
     inp = make_inputs(shape, device="cuda")
     moe = mm.MegaMoE.from_shape(shape, flags=mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0)
@@ -155,7 +160,8 @@ def main():
     if status:
         raise SystemExit(f"device status {status:#x} after the timed steps")
 
-    w = algorithmic(shape, R, N)
+    shared_rows = inp["tokens_per_shard"][shape.local_rank] if shape.num_shared_experts else 0
+    w = algorithmic(shape, R, N, shared_rows)
     st = dict(zip(mm.STAGE_NAMES, stage_ms))
     fused = st["fill"] == 0.0       # the fill ran inside GEMM1's launch and is timed with it
     g1_tflops = w["gemm1_flop"] / (st["gemm1"] * 1e-3) / 1e12
@@ -178,7 +184,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "routed_rows": R, "tokens": N,
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + (
+                       f", plus a shared expert on shard {shape.local_rank}'s {shared_rows} tokens"
+                       if shape.num_shared_experts else ""), "routed_rows": R, "tokens": N,
                    "parallelism": "one GPU's EP share, source ranks emulated as shards"},
         "gemm_pct_fp8_peak": 100.0 * gemm_tflops / FP8_PEAK_TFLOPS,
         "gemm_tflops": gemm_tflops,

@@ -60,7 +60,7 @@ class mega_moe_config(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("num_local_experts", ctypes.c_int32),
                 ("local_rank", ctypes.c_int32), ("topk", ctypes.c_int32), ("block_m", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("num_shared_experts", ctypes.c_int32)]
 
 
 _LAYOUT_U64 = ("status", "chunk_hist", "chunk_base", "send", "recv", "recv_tot", "pool_off", "block_expert",
@@ -135,9 +135,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(num_shards, max_tokens_per_shard, hidden, intermediate, num_experts, num_local_experts,
-                topk, block_m=0, local_rank=0, flags=0) -> mega_moe_config:
+                topk, block_m=0, local_rank=0, flags=0, num_shared_experts=0) -> mega_moe_config:
     return mega_moe_config(num_shards, max_tokens_per_shard, hidden, intermediate, num_experts,
-                           num_local_experts, local_rank, topk, block_m, flags)
+                           num_local_experts, local_rank, topk, block_m, flags, num_shared_experts)
 
 
 # --------------------------------------------------------------- the C entry points, same names
@@ -220,10 +220,10 @@ class MegaMoE:
     """Owns a workspace tensor and a handle; checks tensor shapes and dtypes before each call."""
 
     def __init__(self, num_shards, max_tokens_per_shard, hidden, intermediate, num_experts, num_local_experts,
-                 topk, block_m=0, local_rank=0, flags=0, device="cuda", stream=None):
+                 topk, block_m=0, local_rank=0, flags=0, num_shared_experts=0, device="cuda", stream=None):
         import torch
         self.cfg = make_config(num_shards, max_tokens_per_shard, hidden, intermediate, num_experts,
-                               num_local_experts, topk, block_m, local_rank, flags)
+                               num_local_experts, topk, block_m, local_rank, flags, num_shared_experts)
         self.nbytes = mega_moe_workspace_bytes(self.cfg)
         self.workspace = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         self.h = mega_moe_init(self.cfg, self.workspace, self.nbytes, stream)
@@ -234,7 +234,7 @@ class MegaMoE:
     def from_shape(cls, shape, flags=0, **kw):
         return cls(shape.num_shards, shape.max_tokens_per_shard, shape.hidden, shape.intermediate,
                    shape.num_experts, shape.num_local_experts, shape.topk, shape.block_m, shape.local_rank,
-                   flags, **kw)
+                   flags, getattr(shape, "num_shared_experts", 0), **kw)
 
     def close(self):
         if self.h is not None:
@@ -251,7 +251,7 @@ class MegaMoE:
         import torch
         c = self.cfg
         S, T, H, I, El, K = (c.num_shards, c.max_tokens_per_shard, c.hidden, c.intermediate,
-                             c.num_local_experts, c.topk)
+                             c.num_local_experts + c.num_shared_experts, c.topk)
         want = [("x", x, (S, T, H), torch.uint8), ("x_sf", x_sf, (S, T, H // 128), torch.float32),
                 ("topk_idx", topk_idx, (S, T, K), torch.int64),
                 ("topk_weights", topk_weights, (S, T, K), torch.float32),
@@ -270,14 +270,15 @@ class MegaMoE:
     def packed_shapes(self):
         """Shapes of the packed W1 and W2 (see mega_moe_pack_weights)."""
         c = self.cfg
-        El, H, I = c.num_local_experts, c.hidden, c.intermediate
+        El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
         return (El, I // 128, H // 128, 256, 128), (El, H // 256, I // 128, 256, 128)
 
     def pack_weights(self, w1, w2, stream=None):
-        """Row-major W1 [E_l,2I,H] and W2 [E_l,H,I] (uint8 e4m3fn) -> new packed tensors (w1p, w2p)."""
+        """Row-major W1 [E_w,2I,H] and W2 [E_w,H,I] (uint8 e4m3fn; E_w = E_l + shared experts, the shared
+        expert last) -> new packed tensors (w1p, w2p)."""
         import torch
         c = self.cfg
-        El, H, I = c.num_local_experts, c.hidden, c.intermediate
+        El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
         for name, t, shape in (("w1", w1, (El, 2 * I, H)), ("w2", w2, (El, H, I))):
             if tuple(t.shape) != shape or t.dtype != torch.uint8 or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"{name}: want contiguous cuda uint8 {shape}, got {t.dtype} {tuple(t.shape)}")

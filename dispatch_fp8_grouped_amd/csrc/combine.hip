@@ -4,7 +4,9 @@
 // in ascending k ("Dispatch/Combine: blog theory vs DeepEP vs DeepGEMM Mega MoE", section 1: the output
 // is the weight-sum of the chosen experts' outputs; "DeepGEMM Mega MoE symmetric memory deep analysis",
 // 9.2: per token the top-k slots with a negative index are masked, the rest are accumulated in fp32 and
-// cast to bf16).  A token with no local expert gets a zero row; rows t >= T_s are left untouched.
+// cast to bf16).  With a shared expert, tokens of the own shard also add combine slot K with weight 1,
+// after the routed slots (same page, 8.2 and 9.2: the lane after the top-k lanes stands for the shared
+// slot).  A token with nothing to add gets a zero row; rows t >= T_s are left untouched.
 //
 // One wave per token: lanes 0..K-1 read the token's expert ids and weights and a ballot gives the
 // local slots.  Lane l owns the 16-byte chunks l, l+64, ... of the row; a batch of kBatch chunks is
@@ -49,6 +51,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p) {
         const int64_t e = p.topk_idx[tok * p.K + lane];
         is_local = e >= p.lo && e < p.lo + p.El;
         if (is_local) w = p.topk_w[tok * p.K + lane];
+    } else if (lane == p.K && p.nsh && s == p.own) {
+        is_local = true;
+        w = 1.0f;
     }
     const uint64_t mask = __ballot(is_local);
     const int H8 = p.H >> 3;                        // 16-byte chunks per row

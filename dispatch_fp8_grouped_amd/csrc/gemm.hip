@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // wave*SA_LANES + l, then the wave's two weight-block scales, then (GEMM2) the rows' scatter targets
     __shared__ __attribute__((aligned(16))) uint32_t sSmall[kStages][NW * 64];
     __shared__ float sRed[BM][NWN];
-    __shared__ int sOff[MEGA_MOE_MAX_LOCAL_EXPERTS + 1];
+    __shared__ int sOff[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -369,7 +369,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 
     // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
     // waits on a global load of its own
-    for (int i = tid; i <= p.El; i += NW * 64) sOff[i] = p.pool_off[i];
+    const int nseg = p.El + p.nsh;              // pool segments: routed experts, then the shared one
+    for (int i = tid; i <= nseg; i += NW * 64) sOff[i] = p.pool_off[i];
     __syncthreads();
 
     // Tile t -> pool block, n tile and local expert.  Tiles are numbered expert by expert (expert le
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
         const int t = logical + j * G;
         const int vb = t / NT;
-        int lo = 0, hi = p.El;              // the expert with off[le] <= vb < off[le+1]
+        int lo = 0, hi = nseg;              // the expert with off[le] <= vb < off[le+1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (sOff[mid] <= vb) lo = mid; else hi = mid;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             // eight whole lines each.  Every lane stores (padding rows, target all ones, into the
             // spare row after the K*S*T_max combine rows), so the wave issues exactly kEpiStores
             // stores and no branch splits them.
-            const uint32_t comb_rows = (uint32_t)(p.K * p.S * p.T_max);
+            const uint32_t comb_rows = (uint32_t)((p.K + p.nsh) * p.S * p.T_max);
             const bool odd = rr & 1;
             const size_t col0 = (size_t)nt * 256 + wn * WROWS;
             const uint32_t byte_off = (uint32_t)g * 32 + (odd ? 16u : 0u);

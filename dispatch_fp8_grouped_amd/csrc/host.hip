@@ -58,8 +58,12 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->flags & ~(MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT | MEGA_MOE_FLAG_FILL_IN_GEMM1)) return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
+    // the shared expert reads the own shard and takes combine slot K (a lane of the combine's ballot)
+    if (c->num_shared_experts < 0 || c->num_shared_experts > 1) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->num_shared_experts && (c->local_rank >= c->num_shards || c->topk >= 64)) return MEGA_MOE_ERR_UNSUPPORTED;
     // pool rows and combine rows (K*S*T_max) are int32 / uint32 indices in the kernels
-    if ((int64_t)c->num_shards * c->max_tokens_per_shard * c->topk + (int64_t)c->num_local_experts * 128 >=
+    if ((int64_t)c->num_shards * c->max_tokens_per_shard * (c->topk + 1) + (int64_t)c->num_local_experts * 128 +
+            (int64_t)c->max_tokens_per_shard + 128 >=
         (int64_t)1 << 31)
         return MEGA_MOE_ERR_UNSUPPORTED;
     return MEGA_MOE_OK;
@@ -80,7 +84,8 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     const uint64_t chunks = (T * K + mm::kRouteChunk - 1) / mm::kRouteChunk;
     const uint64_t kloc = K < El ? K : El;
     const uint64_t max_routed = S * T * kloc;
-    const uint64_t max_blocks = (max_routed + bm - 1) / bm + El;
+    const uint64_t nsh = (uint64_t)c->num_shared_experts;
+    const uint64_t max_blocks = (max_routed + bm - 1) / bm + El + nsh * ((T + bm - 1) / bm);
     const uint64_t rows = max_blocks * bm;
     L->block_m = bm;
     L->route_chunks = (int32_t)chunks;
@@ -93,7 +98,7 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->send = take(S * E * 4);
     L->recv = take(El * S * 4);
     L->recv_tot = take(El * 4);
-    L->pool_off = take((El + 1) * 4);
+    L->pool_off = take((El + 2) * 4);
     L->block_expert = take(max_blocks * 4);
     L->block_index = take(max_blocks * 4);
     L->table = take(El * S * T * 4);
@@ -103,7 +108,7 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->pool_dst = take(rows * 4);
     L->l2_x = take(rows * I);
     L->l2_sf = take(rows * (I / 128) * 4);
-    L->comb = take((K * S * T + 1) * H * 2);     // + one spare row: GEMM2 stores padding rows there
+    L->comb = take(((K + nsh) * S * T + 1) * H * 2);   // + one spare row: GEMM2 stores padding rows there
     L->gemm1_out = (c->flags & MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) ? take(rows * 2 * I * 4) : 0;
     L->sched = take((mm::kSchedArrival + max_blocks) * 4);
     L->total = o;
@@ -162,7 +167,8 @@ int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const 
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MEGA_MOE_ERR_HIP;
-    if (mm::launch_pack(w1, w2, w1_packed, w2_packed, cfg->num_local_experts, cfg->hidden, cfg->intermediate, cus,
+    if (mm::launch_pack(w1, w2, w1_packed, w2_packed, cfg->num_local_experts + cfg->num_shared_experts, cfg->hidden,
+                        cfg->intermediate, cus,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
         return MEGA_MOE_ERR_HIP;
     return MEGA_MOE_OK;
@@ -233,6 +239,8 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
     p.I = c.intermediate;
     p.E = c.num_experts;
     p.El = c.num_local_experts;
+    p.nsh = c.num_shared_experts;
+    p.own = c.local_rank;
     p.lo = c.local_rank * c.num_local_experts;
     p.K = c.topk;
     p.BM = h->lay.block_m;

@@ -22,6 +22,8 @@ constexpr int kSchedArrival = 64;      // [kSchedArrival + b]: completed fill un
 struct Params {
     // shapes
     int S, T_max, H, I, E, El, lo, K, BM;
+    int nsh;              // shared experts (0 or 1): pool segment El, weights index El, combine slot K
+    int own;              // the shard the shared expert reads (local_rank)
     int chunks;           // routing chunks per shard
     int max_blocks;       // pool capacity in BM blocks
     uint32_t flags;

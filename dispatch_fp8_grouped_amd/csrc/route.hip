@@ -89,11 +89,17 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(Params p) {
 }
 
 // One work-group: recv_tot, the cumulative statistics, expert-major pool offsets ("Mega-MoE notes,
-// part 2: index table and pull", 2.4), the block count and the block list.
+// part 2: index table and pull", 2.4), the block count and the block list.  With a shared expert, one
+// more segment follows the routed ones: the valid tokens of the own shard in order, with top-k slot K
+// ("DeepGEMM Mega MoE symmetric memory deep analysis", 4.1: the shared expert reads the rank's own
+// input buffer; 8.2: its output takes the extra combine slot K); this kernel writes that segment's
+// metadata and scatter targets too.
 __global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
     __shared__ int s_tot[MEGA_MOE_MAX_LOCAL_EXPERTS];
-    __shared__ int s_off[MEGA_MOE_MAX_LOCAL_EXPERTS + 1];
+    __shared__ int s_off[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
     const int tid = threadIdx.x;
+    const int nseg = p.El + p.nsh;                  // pool segments: routed experts, then the shared one
+    const int n_own = p.nsh ? p.tps[p.own] : 0;
     for (int le = tid; le < p.El; le += 1024) {
         int t = 0;
         for (int s = 0; s < p.S; ++s) t += p.recv[le * p.S + s];
@@ -111,18 +117,35 @@ __global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
         }
         s_off[p.El] = o;
         p.pool_off[p.El] = o;
+        o += (n_own + p.BM - 1) / p.BM;             // the shared segment (empty without one)
+        s_off[p.El + 1] = o;
+        p.pool_off[p.El + 1] = o;
         p.status[1] = (uint32_t)o;
     }
     __syncthreads();
-    const int nb = min(s_off[p.El], p.max_blocks);   // never below s_off[El]: the pool holds every row
+    const int nb = min(s_off[nseg], p.max_blocks);   // never below s_off[nseg]: the pool holds every row
     for (int b = tid; b < nb; b += 1024) {
-        int lo = 0, hi = p.El;            // last le with s_off[le] <= b: the non-empty owner of b
+        int lo = 0, hi = nseg;            // last segment with s_off[le] <= b: the non-empty owner of b
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (s_off[mid] <= b) lo = mid; else hi = mid;
         }
         p.block_expert[b] = lo;
         p.block_index[b] = b - s_off[lo];
+    }
+    if (p.nsh) {
+        // shared segment: row off*BM + t holds token t of the own shard, k = K; the rest of its last
+        // block is padding (all ones)
+        const size_t r0 = (size_t)s_off[p.El] * p.BM;
+        const size_t r1 = min((size_t)s_off[p.El + 1] * p.BM, (size_t)p.max_blocks * p.BM);
+        for (size_t r = r0 + tid; r < r1; r += 1024) {
+            const int t = (int)(r - r0);
+            const bool ok = t < n_own;
+            p.pool_meta[r * 3] = ok ? (uint32_t)p.own : kMetaPad;
+            p.pool_meta[r * 3 + 1] = ok ? (uint32_t)t : kMetaPad;
+            p.pool_meta[r * 3 + 2] = ok ? (uint32_t)p.K : kMetaPad;
+            p.pool_dst[r] = ok ? (uint32_t)(((size_t)p.K * p.S + p.own) * p.T_max + t) : kMetaPad;
+        }
     }
 }
 

@@ -92,6 +92,13 @@ typedef struct mega_moe_config {
     int32_t topk;                 /* K: 1..64                                                           */
     int32_t block_m;              /* BLOCK_M of the pool: 64 or 128; 0 picks from the expected rows     */
     uint32_t flags;               /* MEGA_MOE_FLAG_*                                                    */
+    int32_t num_shared_experts;   /* 0 or 1.  1: a shared expert (intermediate size I, weights stored   */
+                                  /* as expert E_l of W1/W2) runs on every valid token of this rank's   */
+                                  /* own shard, shard local_rank (needs local_rank < S and K < 64), and */
+                                  /* its output is added with weight 1 after the routed slots           */
+                                  /* ("DeepGEMM Mega MoE symmetric memory deep analysis", 4.1, 8.1-8.2, */
+                                  /* 9.2: the shared expert reads the rank's own input buffer and        */
+                                  /* writes the extra combine slot K locally)                           */
 } mega_moe_config;
 
 /* Byte offsets of the regions inside the workspace (for tests and tools) plus the resolved sizes. */
@@ -99,6 +106,7 @@ typedef struct mega_moe_layout {
     int32_t block_m;          /* resolved BLOCK_M                                                 */
     int32_t route_chunks;     /* routing chunks per shard                                         */
     int32_t max_pool_blocks;  /* capacity in BLOCK_M blocks: ceil(S*T_max*min(K,E_l)/BM) + E_l     */
+                              /*   (+ ceil(T_max/BM) with a shared expert)                          */
     int32_t reserved;
     uint64_t status;          /* uint32 [0]: status bits; uint32 [1]: number of pool blocks (last forward) */
     uint64_t chunk_hist;      /* int32 [S][chunks][E]                                             */
@@ -106,7 +114,9 @@ typedef struct mega_moe_layout {
     uint64_t send;            /* int32 [S][E]: pairs of shard s routed to global expert e         */
     uint64_t recv;            /* int32 [E_l][S]: recv[le][s] = send[s][r*E_l+le]                  */
     uint64_t recv_tot;        /* int32 [E_l]                                                      */
-    uint64_t pool_off;        /* int32 [E_l+1]: first pool block of each local expert             */
+    uint64_t pool_off;        /* int32 [E_l+2]: first pool block of each local expert; [E_l] ends */
+                              /*   the routed segments, [E_l+1] the shared expert's segment (the    */
+                              /*   own shard's valid tokens in order; equal to [E_l] without one)  */
     uint64_t block_expert;    /* int32 [max_pool_blocks]: local expert of each pool block          */
     uint64_t block_index;     /* int32 [max_pool_blocks]: m-block index inside its expert          */
     uint64_t table;           /* int32 [E_l][S][T_max]: t*K+k, slots >= recv[le][s] unspecified    */
@@ -121,8 +131,9 @@ typedef struct mega_moe_layout {
     uint64_t l2_x;            /* uint8 [max_pool_blocks][I/128][4][BM][32] e4m3fn: per block and K  */
                               /* block, four 32-column quarters of BM rows                        */
     uint64_t l2_sf;           /* float [max_pool_blocks][I/128][BM], block-major like pool_sf      */
-    uint64_t comb;            /* bf16 [K][S*T_max][H]: rows of routed (k, shard, token) only, then  */
-                              /* one spare row that takes GEMM2's padding rows                   */
+    uint64_t comb;            /* bf16 [K + n_shared][S*T_max][H]: rows of routed (k, shard, token) */
+                              /* (plane K: the shared expert's rows of the own shard), then one    */
+                              /* spare row that takes GEMM2's padding rows                        */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
     uint64_t sched;           /* uint32 [64 + max_pool_blocks]: FILL_IN_GEMM1 schedule: [0] next     */
                               /*   fill unit to claim, [1] units done, [2] exit ticket, [64 + b]   */
@@ -147,12 +158,13 @@ int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t work
 /* One-time weight transform (the pages' kernels take their weights in a transformed layout too:
  * "DeepGEMM Mega MoE symmetric memory deep analysis", 10.2).  Copies W1 and W2 into the tiled order the
  * grouped GEMMs stream, where one K step of one n tile is one contiguous 32 KB chunk:
- *   w1_packed  uint8 [E_l][I/128][H/128][256][128]: chunk (le, nt, kb), row r, byte j holds
+ * E_w = E_l + num_shared_experts experts are packed (the shared expert last).
+ *   w1_packed  uint8 [E_w][I/128][H/128][256][128]: chunk (le, nt, kb), row r, byte j holds
  *              W1[le][r < 128 ? nt*128 + r : I + nt*128 + r - 128][kb*128 + j]   (128 gate rows, then
  *              the matching 128 up rows)
- *   w2_packed  uint8 [E_l][H/256][I/128][256][128]: chunk (le, nt, kb), row r, byte j holds
+ *   w2_packed  uint8 [E_w][H/256][I/128][256][128]: chunk (le, nt, kb), row r, byte j holds
  *              W2[le][nt*256 + r][kb*128 + j]
- * w1 / w2 are the row-major [E_l][2I][H] / [E_l][H][I] e4m3fn tensors below; the packed buffers have the
+ * w1 / w2 are the row-major [E_w][2I][H] / [E_w][H][I] e4m3fn tensors below; the packed buffers have the
  * same byte counts and must not overlap them.  Asynchronous on `stream`; no handle is needed.
  * Errors: INVALID_ARG (null or not 16-byte aligned pointer), UNSUPPORTED (config), HIP. */
 int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const void* w2, void* w1_packed,
@@ -165,13 +177,14 @@ int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const 
  *   x_sf              float [S][T_max][H/128], per-token per-128-column scales
  *   topk_idx          int64 [S][T_max][K], global expert ids; < 0 means "no expert"
  *   topk_weights      float [S][T_max][K]
- *   w1                W1 packed by mega_moe_pack_weights from uint8 [E_l][2I][H] e4m3fn (rows 0..I-1
- *                     gate, I..2I-1 up)
- *   w1_sf             float [E_l][2I/128][H/128], 128x128 block scales of the unpacked W1
- *   w2                W2 packed by mega_moe_pack_weights from uint8 [E_l][H][I] e4m3fn
- *   w2_sf             float [E_l][H/128][I/128]
+ *   w1                W1 packed by mega_moe_pack_weights from uint8 [E_w][2I][H] e4m3fn (rows 0..I-1
+ *                     gate, I..2I-1 up; E_w = E_l + num_shared_experts, the shared expert last)
+ *   w1_sf             float [E_w][2I/128][H/128], 128x128 block scales of the unpacked W1
+ *   w2                W2 packed by mega_moe_pack_weights from uint8 [E_w][H][I] e4m3fn
+ *   w2_sf             float [E_w][H/128][I/128]
  *   y                 bf16 [S][T_max][H] output: y[s,t] = sum over k with a local expert of
- *                     w[s,t,k] * Expert(x[s,t]); a token with no local expert gets a zero row
+ *                     w[s,t,k] * Expert(x[s,t]), plus Shared(x[s,t]) for s = local_rank when the
+ *                     config has a shared expert; a token with nothing to add gets a zero row
  *   cum_recv_stats    int32 [E_l] or NULL: cum_recv_stats[le] += rows received by local expert le
  *                     (the caller resets it; "DeepGEMM Mega MoE symmetric memory deep analysis", 10.1)
  * Errors: INVALID_ARG, TOO_MANY_TOKENS, HIP.  Leaves the workspace ready for the next call. */

@@ -39,6 +39,7 @@ class Run:
     def layout_host(self):
         sh, L = self.shape, self.moe.layout
         S, T, E, El = sh.num_shards, sh.max_tokens_per_shard, sh.num_experts, sh.num_local_experts
+        nsh = getattr(sh, "num_shared_experts", 0)
         status = self.region("status", torch.int32, (2,)).cpu().numpy()
         nb = int(status[1])
         out = dict(
@@ -46,7 +47,7 @@ class Run:
             send=self.region("send", torch.int32, (S, E)).cpu().numpy(),
             recv=self.region("recv", torch.int32, (El, S)).cpu().numpy(),
             recv_tot=self.region("recv_tot", torch.int32, (El,)).cpu().numpy(),
-            pool_off=self.region("pool_off", torch.int32, (El + 1,)).cpu().numpy(),
+            pool_off=self.region("pool_off", torch.int32, (El + 2,)).cpu().numpy()[:El + 1 + nsh],
             block_expert=self.region("block_expert", torch.int32, (L["max_pool_blocks"],)).cpu().numpy()[:nb],
             block_index=self.region("block_index", torch.int32, (L["max_pool_blocks"],)).cpu().numpy()[:nb],
             table=self.region("table", torch.int32, (El, S, T)).cpu().numpy(),
@@ -110,18 +111,23 @@ class Run:
 
 
 def check_layout(run, inp_np, ref=None):
-    """Counts, table, offsets, block list and the whole pool: bit-exact against the oracle."""
+    """Counts, table, offsets, block list and the whole pool: bit-exact against the oracle.
+    With a shared expert the offsets, block list and pool include its segment."""
     sh = run.shape
+    nsh = getattr(sh, "num_shared_experts", 0)
     rt = oracle.route(inp_np["topk_idx"], inp_np["tokens_per_shard"], sh.num_experts,
                       sh.num_local_experts, sh.local_rank)
     got = run.layout_host()
     assert np.array_equal(got["send"], rt.send), "send counts"
     assert np.array_equal(got["recv"], rt.recv), "recv counts"
     assert np.array_equal(got["recv_tot"], rt.recv_tot), "recv_tot"
-    off = oracle.pool_offsets(rt.recv_tot, run.moe.block_m)
+    px, psf, pm, off = oracle.fill_pool(inp_np["x"], inp_np["x_sf"], rt, run.moe.block_m, sh.topk,
+                                        shared_shard=sh.local_rank if nsh else None,
+                                        shared_tokens=inp_np["tokens_per_shard"][sh.local_rank] if nsh else 0)
+    assert np.array_equal(off[:sh.num_local_experts + 1], oracle.pool_offsets(rt.recv_tot, run.moe.block_m))
     assert np.array_equal(got["pool_off"], off), "pool offsets"
     assert got["nblocks"] == off[-1]
-    want_be = np.repeat(np.arange(sh.num_local_experts), np.diff(off))
+    want_be = np.repeat(np.arange(len(off) - 1), np.diff(off))
     want_bi = np.concatenate([np.arange(n) for n in np.diff(off)]) if off[-1] else np.zeros(0, np.int64)
     assert np.array_equal(got["block_expert"], want_be), "block -> expert"
     assert np.array_equal(got["block_index"], want_bi), "block index in expert"
@@ -129,7 +135,6 @@ def check_layout(run, inp_np, ref=None):
         for s in range(sh.num_shards):
             n = rt.recv[le, s]
             assert np.array_equal(got["table"][le, s, :n], rt.table[le, s, :n]), ("table", le, s)
-    px, psf, pm, _ = oracle.fill_pool(inp_np["x"], inp_np["x_sf"], rt, run.moe.block_m, sh.topk)
     gx, gsf, gm = run.pool_host()
     assert gx.shape == px.shape
     assert np.array_equal(gm, pm), "pool metadata"

@@ -127,3 +127,28 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("the oracle", ""), f
                 assert "import inputs" not in text, f
+
+
+def test_shared_expert_config_and_workspace():
+    """A shared expert adds one pool segment of ceil(T_max/BM) blocks and one combine plane; it needs the
+    own shard to exist and a free lane after the top-k lanes."""
+    base = mm.mega_moe_workspace_bytes(cfg_of("decode"))
+    sh = SHAPES["decode"]
+    n = mm.mega_moe_workspace_bytes(cfg_of("decode", num_shared_experts=1))
+    plane = sh.num_shards * sh.max_tokens_per_shard * sh.hidden * 2
+    extra_rows = -(-sh.max_tokens_per_shard // sh.block_m) * sh.block_m
+    assert n >= base + plane + extra_rows * (sh.hidden + sh.intermediate)
+    lib = mm.lib()
+    import ctypes
+    # 2 shards, 8 ranks' worth of experts: rank 5 is a valid owner but has no own shard among the 2
+    two = dict(num_shards=2, max_tokens_per_shard=64, hidden=256, intermediate=128, num_experts=64,
+               num_local_experts=8, topk=4, block_m=64)
+    out = ctypes.c_uint64(0)
+    c = mm.make_config(**two, local_rank=5)
+    assert lib.mega_moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == mm.OK
+    cases = [mm.make_config(**two, local_rank=5, num_shared_experts=1),
+             cfg_of("decode", num_shared_experts=2), cfg_of("decode", num_shared_experts=-1),
+             cfg_of("decode", num_shared_experts=1, topk=64)]          # no lane left for slot K
+    for c in cases:
+        assert lib.mega_moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == mm.ERR_UNSUPPORTED
+    assert lib.mega_moe_workspace_bytes(ctypes.byref(cfg_of("decode", topk=64)), ctypes.byref(out)) == mm.OK

@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 def _whole(run, inp):
     sh = run.shape
-    ref = oracle.forward(inp, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m)
+    ref = oracle.forward(inp, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m,
+                         num_shared_experts=sh.num_shared_experts)
     y = run.y_host()
     valid = ~np.isnan(ref["y"])
     tol_check(y[valid], ref["y"][valid], sh.name)

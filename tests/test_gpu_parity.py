@@ -31,7 +31,8 @@ def full_compare(shape, inputs=None, flags=0, name=""):
     inp = inputs_np(run)
     assert run.status == 0
     check_layout(run, inp)
-    ref = oracle.forward(inp, shape.num_experts, shape.num_local_experts, shape.local_rank, shape.block_m)
+    ref = oracle.forward(inp, shape.num_experts, shape.num_local_experts, shape.local_rank, shape.block_m,
+                         num_shared_experts=shape.num_shared_experts)
     y = run.y_host()
     valid = ~np.isnan(ref["y"])
     tol_check(y[valid], ref["y"][valid], name)
@@ -63,10 +64,25 @@ def test_bm128_ragged_tail():
     full_compare(sh, inputs=inp, name="bm128")
 
 
+# --------------------------------------------------------------- shared expert
+@pytest.mark.parametrize("case", ["bm64_rank1", "bm128_rank0"])
+def test_shared_expert_whole_layer(case):
+    """A shared expert on the own shard's tokens (pool segment after the routed experts, combine slot
+    K, weight 1): layout bit-exact, whole output within tolerance."""
+    if case == "bm64_rank1":
+        sh = MoEShape("shared64", 3, 150, 512, 256, 16, 8, 4, 64, local_rank=1, num_shared_experts=1, seed=51)
+        tps = [150, 97, 3]
+    else:
+        sh = MoEShape("shared128", 2, 300, 768, 384, 8, 4, 2, 128, local_rank=0, num_shared_experts=1, seed=52)
+        tps = [257, 300]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    full_compare(sh, inputs=inp, name=sh.name)
+
+
 # --------------------------------------------------------------- full sizes, sampled values
-@pytest.mark.parametrize("name", ["decode", "skewed", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "skewed", "prefill", "decode_shared"])
 def test_full_size_layout_and_sampled_tokens(name):
-    shape = SHAPES[name]
+    shape = SHAPES[name] if name in SHAPES else SHAPES["decode"].replace(name=name, num_shared_experts=1)
     _print_case(name, shape)
     run = Run(shape)
     inp = inputs_np(run)
@@ -75,8 +91,11 @@ def test_full_size_layout_and_sampled_tokens(name):
     y = run.y_host()
     cache = {}
     toks = sample_tokens(inp, shape, 12, seed=shape.seed)
+    if shape.num_shared_experts:
+        toks += [(shape.local_rank, t) for t in (0, 77, shape.max_tokens_per_shard - 1)]
     got = np.stack([y[s, t] for s, t in toks])
-    want = np.stack([oracle.direct_token(inp, s, t, shape.num_local_experts, shape.local_rank, cache=cache)
+    want = np.stack([oracle.direct_token(inp, s, t, shape.num_local_experts, shape.local_rank, cache=cache,
+                                         num_shared_experts=shape.num_shared_experts)
                      for s, t in toks])
     tol_check(got, want, f"{name} sampled y")
     # padding and unrouted rows of y: tokens without local experts are exact zeros
