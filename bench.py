@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-experts", type=int, default=0, choices=(0, 1),
                     help="add a shared expert on the own shard's tokens (pool segment + combine slot K)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one forward in a HIP graph and time its replays (same kernels, fewer "
+                         "host launches)")
     ap.add_argument("--fill-in-gemm1", action="store_true",
                     help="pull the pool rows inside GEMM1's launch, GEMM1 waiting on per-block arrival counts "
                          "(default: the fill is its own kernel, stream-ordered before GEMM1)")
@@ -142,19 +145,41 @@ def main():
     R = int(recv_tot.sum())
     N = sum(inp["tokens_per_shard"])
 
-    mm.mega_moe_set_timing(moe.h, True)
+    graph = None
+    if args.graph:
+        # one forward captured (stage timing off: its events would be frozen into the graph)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe(inp, y=y)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        stage_ms = None
+    else:
+        mm.mega_moe_set_timing(moe.h, True)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        moe(inp, y=y)
+        if graph is not None:
+            graph.replay()
+        else:
+            moe(inp, y=y)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
-    stage_ms, nt = mm.mega_moe_stage_times(moe.h, with_count=True)
-    mm.mega_moe_set_timing(moe.h, False)
-    assert nt == args.steps
+    if graph is None:
+        stage_ms, nt = mm.mega_moe_stage_times(moe.h, with_count=True)
+        mm.mega_moe_set_timing(moe.h, False)
+        assert nt == args.steps
+    else:
+        # per-stage times from an eager timed pass (the graph replays the same kernels)
+        mm.mega_moe_set_timing(moe.h, True)
+        for _ in range(min(args.steps, 10)):
+            moe(inp, y=y)
+        stage_ms = mm.mega_moe_stage_times(moe.h)
+        mm.mega_moe_set_timing(moe.h, False)
     ms = ms_total / args.steps
     status = moe.status()
     if status:
@@ -196,7 +221,8 @@ def main():
                      "frac": g1_tflops / FP8_PEAK_TFLOPS, "traffic": measured_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic": "4*R*H*I flop per launch, R = routed rows"},
-        "schedule": "fill inside gemm1" if fused else "stream-ordered fill kernel",
+        "schedule": ("fill inside gemm1" if fused else "stream-ordered fill kernel") +
+                    (", forward replayed from a HIP graph" if graph is not None else ""),
         "stages_ms": st,
         "stages": {
             "route": {"GB/s": gbs(w["route_bytes"], st["route"])},

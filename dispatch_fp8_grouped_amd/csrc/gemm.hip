@@ -279,12 +279,15 @@ __device__ __forceinline__ void fill_pool(const Params& p, int nblocks, int lane
 
 // Bounded spin (per wave) until *word reaches `target`; every poll is a device-scope acquire, so polls
 // are spaced by a sleep.  A wait longer than kSpinTicks latches TIMEOUT and gives up: never expected,
-// it keeps a broken schedule from hanging the GPU.
+// it keeps a broken schedule from hanging the GPU.  MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT makes every wait
+// give up as soon as the clock moves, so tests reach that path from the host.
 __device__ __forceinline__ void spin_until(const Params& p, const uint32_t* word, uint32_t target, int lane) {
-    if (sched_load(word) >= target) return;
+    const bool force = p.flags & MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT;
+    if (!force && sched_load(word) >= target) return;
+    const long long limit = force ? 0 : kSpinTicks;
     const long long t0 = wall_clock64();
-    while (sched_load(word) < target) {
-        if (wall_clock64() - t0 > kSpinTicks) {
+    while (force || sched_load(word) < target) {
+        if (wall_clock64() - t0 > limit) {
             if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_TIMEOUT);
             return;
         }

@@ -68,6 +68,10 @@ extern "C" {
                                                   on those counts instead of a kernel boundary.  Same
                                                   results bit for bit; slower on MI355X (each published unit
                                                   costs a device-scope L2 writeback), so off by default */
+#define MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT 0x4u /* tests: with FILL_IN_GEMM1, every bounded wait gives up at
+                                                  once and latches MEGA_MOE_STATUS_TIMEOUT (the kernel
+                                                  still exits normally and zeroes its schedule words; the
+                                                  output is undefined) */
 
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
 #define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */

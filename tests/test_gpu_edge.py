@@ -291,3 +291,63 @@ def test_fill_inside_gemm1_matches_separate_fill(case):
     _whole(a, n)
     for r in runs:
         r.close()
+
+
+def test_graph_capture_replays_match_eager():
+    """One forward captured in a HIP graph: three replays on changing input contents, with eager
+    forwards and synchronisations between them, each bit-identical to the eager forward on the same
+    inputs (the forward records no memset and leaves its workspace counters at zero)."""
+    print("[case] graph capture and replays", flush=True)
+    sh = MoEShape("graph", 4, 96, 512, 256, 32, 8, 4, 64, local_rank=1, seed=61)
+    tps = [96, 50, 0, 77]
+    a = on_gpu(make_inputs(sh, tokens_per_shard=tps))
+    b = on_gpu(make_inputs(sh, seed=62, tokens_per_shard=tps))
+    for k in ("w1", "w1_sf", "w2", "w2_sf"):
+        b[k] = a[k]
+    moe = mm.MegaMoE.from_shape(sh)
+    moe(a)                                   # packs a's weights into a["w1_packed"], a["w2_packed"]
+    b["w1_packed"], b["w2_packed"] = a["w1_packed"], a["w2_packed"]
+    ya, yb = moe(a), moe(b)
+    torch.cuda.synchronize()
+    dyn = ("x", "x_sf", "topk_idx", "topk_weights")
+    static = dict(a)
+    for k in dyn:
+        static[k] = a[k].clone()
+    y = torch.zeros_like(ya)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe(static, y=y)
+    def same(u, v):                          # rows t >= T_s are never written: compare valid rows
+        return all(torch.equal(u[i, :n].view(torch.int16), v[i, :n].view(torch.int16)) for i, n in enumerate(tps))
+    for src, want in ((a, ya), (b, yb), (a, ya)):
+        for k in dyn:
+            static[k].copy_(src[k])
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(y, want)
+        other = moe(b)                       # eager work between replays
+        torch.cuda.synchronize()
+        assert same(other, yb)
+    assert moe.status() == 0
+    del g
+    moe.close()
+
+
+def test_forced_timeout_latches_status_and_recovers():
+    """The arrival-counted schedule's bounded waits, forced from the host to give up at once: the
+    status word reports TIMEOUT, the launch still completes and zeroes its schedule words, and a
+    normal handle on the same inputs is unaffected."""
+    print("[case] forced wait timeout", flush=True)
+    sh = MoEShape("tmo", 2, 80, 256, 128, 8, 4, 2, 64, seed=71)
+    inp = on_gpu(make_inputs(sh))
+    forced = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_DEBUG_FORCE_TIMEOUT)
+    for _ in range(2):
+        forced(inp)
+        assert forced.status() == mm.STATUS_TIMEOUT
+        assert not _sched_words(forced).any()
+    forced.close()
+    run = Run(sh, inputs=inp, flags=mm.FLAG_FILL_IN_GEMM1)
+    assert run.status == 0
+    _whole(run, inputs_np(run))
+    run.close()
