@@ -5,14 +5,15 @@
 // ("Mega-MoE kernel code walkthrough: from Dispatch to WGMMA", 4.2), which makes the slot order
 // depend on timing.  Here the same counting sort ("Dispatch/Combine: blog theory vs DeepEP vs DeepGEMM
 // Mega MoE", 4.4: count, prefix sum, scatter) is done deterministically: slots of one (expert, shard)
-// follow ascending t*K+k.  Four launches:
+// follow ascending t*K+k.  Three launches:
 //   route_count  grid (chunks, S): LDS histogram of one chunk of 256 (token, k) entries over all E
 //   route_scan   grid S:           send[s][e], per-chunk slot bases, recv
-//   route_pool   one work-group:   recv_tot, pool offsets ("Mega-MoE notes, part 2: index table and
-//                                  pull", 2.4), block count and block list
-//   route_table  grid (chunks, S), one wave each: stable in-wave ranking by ballot/popcount, writes
-//                table[le][s][slot] = t*K+k ("Mega-MoE notes, part 2", 1.1-1.3) and the entry's pool
-//                row metadata and GEMM2 scatter target (its round-robin position, 2.5), padding rows
+//   route_table  grid (chunks, S), one wave each: the pool offsets from recv ("Mega-MoE notes, part 2:
+//                index table and pull", 2.4; the first work-group also writes recv_tot, the offsets,
+//                the block count and the block list), then a stable in-wave ranking by
+//                ballot/popcount that writes table[le][s][slot] = t*K+k (same page, 1.1-1.3) and the
+//                entry's pool row metadata and GEMM2 scatter target (its round-robin position, 2.5),
+//                padding rows
 #include "mm_internal.h"
 
 namespace mm {
@@ -88,57 +89,68 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(Params p) {
     if (overflow) atomicOr(p.status, MEGA_MOE_STATUS_SLOT_OVERFLOW);
 }
 
-// One work-group: recv_tot, the cumulative statistics, expert-major pool offsets ("Mega-MoE notes,
-// part 2: index table and pull", 2.4), the block count and the block list.  With a shared expert, one
-// more segment follows the routed ones: the valid tokens of the own shard in order, with top-k slot K
-// ("DeepGEMM Mega MoE symmetric memory deep analysis", 4.1: the shared expert reads the rank's own
-// input buffer; 8.2: its output takes the extra combine slot K); this kernel writes that segment's
-// metadata and scatter targets too.
-__global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
-    __shared__ int s_tot[MEGA_MOE_MAX_LOCAL_EXPERTS];
-    __shared__ int s_off[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
-    const int tid = threadIdx.x;
-    const int nseg = p.El + p.nsh;                  // pool segments: routed experts, then the shared one
-    const int n_own = p.nsh ? p.tps[p.own] : 0;
-    for (int le = tid; le < p.El; le += 1024) {
-        int t = 0;
-        for (int s = 0; s < p.S; ++s) t += p.recv[le * p.S + s];
-        s_tot[le] = t;
-        p.recv_tot[le] = t;
-        if (p.cum) p.cum[le] += t;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int o = 0;
-        for (int le = 0; le < p.El; ++le) {
-            s_off[le] = o;
-            p.pool_off[le] = o;
-            o += (s_tot[le] + p.BM - 1) / p.BM;
+// Pool layout from the counts ("Mega-MoE notes, part 2: index table and pull", 2.4: expert-major
+// segments of ceil(recv_tot / BLOCK_M) blocks).  Every routing work-group (one wave) computes the
+// offsets for itself in LDS with a wave prefix sum, so no launch sits between the scan and the table.
+// offs[le] = first block of local expert le, offs[El] = end of the routed segments, offs[El + 1] = end
+// of the shared expert's segment (the own shard's valid tokens; equal to offs[El] without one).
+__device__ __forceinline__ void pool_layout(const Params& p, const int* recv_v, int* offs, int lane) {
+    int carry = 0;
+    for (int le0 = 0; le0 < p.El; le0 += 64) {
+        const int le = le0 + lane;
+        int nb = 0;
+        if (le < p.El) {
+            int tot = 0;
+            for (int sp = 0; sp < p.S; ++sp) tot += recv_v[le * p.S + sp];
+            nb = (tot + p.BM - 1) / p.BM;
         }
-        s_off[p.El] = o;
-        p.pool_off[p.El] = o;
-        o += (n_own + p.BM - 1) / p.BM;             // the shared segment (empty without one)
-        s_off[p.El + 1] = o;
-        p.pool_off[p.El + 1] = o;
-        p.status[1] = (uint32_t)o;
+        int x = nb;                                  // inclusive prefix sum over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (le < p.El) offs[le] = carry + x - nb;
+        carry += __shfl(x, 63);
     }
-    __syncthreads();
-    const int nb = min(s_off[nseg], p.max_blocks);   // never below s_off[nseg]: the pool holds every row
-    for (int b = tid; b < nb; b += 1024) {
-        int lo = 0, hi = nseg;            // last segment with s_off[le] <= b: the non-empty owner of b
+    if (lane == 0) {
+        const int n_own = p.nsh ? p.tps[p.own] : 0;
+        offs[p.El] = carry;
+        offs[p.El + 1] = carry + (n_own + p.BM - 1) / p.BM;
+    }
+}
+
+// Written once per forward (by the first routing work-group): recv_tot, the cumulative statistics, the
+// offsets, the block count and the block list.  With a shared expert, its segment follows the routed
+// ones: the valid tokens of the own shard in order, with top-k slot K ("DeepGEMM Mega MoE symmetric
+// memory deep analysis", 4.1: the shared expert reads the rank's own input buffer; 8.2: its output
+// takes the extra combine slot K); its metadata and scatter targets are written here too.
+__device__ __forceinline__ void pool_publish(const Params& p, const int* recv_v, const int* offs, int lane) {
+    for (int le = lane; le < p.El; le += 64) {
+        int tot = 0;
+        for (int sp = 0; sp < p.S; ++sp) tot += recv_v[le * p.S + sp];
+        p.recv_tot[le] = tot;
+        if (p.cum) p.cum[le] += tot;
+    }
+    for (int i = lane; i <= p.El + 1; i += 64) p.pool_off[i] = offs[i];
+    if (lane == 0) p.status[1] = (uint32_t)offs[p.El + 1];
+    const int nseg = p.El + p.nsh;                   // pool segments: routed experts, then the shared one
+    const int nb = min(offs[nseg], p.max_blocks);    // never below offs[nseg]: the pool holds every row
+    for (int b = lane; b < nb; b += 64) {
+        int lo = 0, hi = nseg;            // last segment with offs[le] <= b: the non-empty owner of b
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (s_off[mid] <= b) lo = mid; else hi = mid;
+            if (offs[mid] <= b) lo = mid; else hi = mid;
         }
         p.block_expert[b] = lo;
-        p.block_index[b] = b - s_off[lo];
+        p.block_index[b] = b - offs[lo];
     }
     if (p.nsh) {
-        // shared segment: row off*BM + t holds token t of the own shard, k = K; the rest of its last
-        // block is padding (all ones)
-        const size_t r0 = (size_t)s_off[p.El] * p.BM;
-        const size_t r1 = min((size_t)s_off[p.El + 1] * p.BM, (size_t)p.max_blocks * p.BM);
-        for (size_t r = r0 + tid; r < r1; r += 1024) {
+        // row off*BM + t holds token t of the own shard, k = K; the rest of the last block is padding
+        const int n_own = p.tps[p.own];
+        const size_t r0 = (size_t)offs[p.El] * p.BM;
+        const size_t r1 = min((size_t)offs[p.El + 1] * p.BM, (size_t)p.max_blocks * p.BM);
+        for (size_t r = r0 + lane; r < r1; r += 64) {
             const int t = (int)(r - r0);
             const bool ok = t < n_own;
             p.pool_meta[r * 3] = ok ? (uint32_t)p.own : kMetaPad;
@@ -160,14 +172,15 @@ __global__ __launch_bounds__(1024) void route_pool_kernel(Params p) {
 // (Round r of the min-peeling covers the slots between two consecutive distinct counts, and the shards
 // active in it are exactly those whose count exceeds the slot.)  The row gets the metadata {s, t, k} and
 // the GEMM2 scatter target k*S*T_max + s*T_max + t; the padding rows of each expert get all ones from
-// one work-group.  recv and pool_off are staged in LDS when they fit (kStageInts), else read from
-// global memory through the same generic pointer.
+// one work-group.  recv is staged in LDS when it fits (kStageInts), else read from global memory
+// through the same generic pointer; the pool offsets are computed from it (pool_layout).
 constexpr int kStageInts = 4096;
 
 template <bool kRegRun>
 __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
     __shared__ int run[kRegRun ? 1 : MEGA_MOE_MAX_LOCAL_EXPERTS];
     __shared__ int stage[kStageInts];
+    __shared__ int offs[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
     const int c = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
     const int* base = p.chunk_base + ((size_t)s * p.chunks + c) * p.El;
     const long n = (long)p.tps[s] * p.K;
@@ -180,35 +193,37 @@ __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
         const long f = f0 + r * 64 + lane;
         e_of[r] = f < n ? idx[f] : -1;
     }
-    const bool staged = p.El * p.S + p.El + 1 <= kStageInts;
+    const bool staged = p.El * p.S <= kStageInts;
     const int* recv_v = p.recv;
-    const int* off_v = p.pool_off;
     if (staged) {
         // up to 8 loads per lane in flight per round (one round for the usual El*S)
-        const int nr = p.El * p.S, n_all = nr + p.El + 1;
-        for (int i0 = 0; i0 < n_all; i0 += 64 * 8) {
+        const int nr = p.El * p.S;
+        for (int i0 = 0; i0 < nr; i0 += 64 * 8) {
             int v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int i = i0 + u * 64 + lane;
-                v[u] = i < nr ? p.recv[i] : i < n_all ? p.pool_off[i - nr] : 0;
+                v[u] = i < nr ? p.recv[i] : 0;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int i = i0 + u * 64 + lane;
-                if (i < n_all) stage[i] = v[u];
+                if (i < nr) stage[i] = v[u];
             }
         }
         recv_v = stage;
-        off_v = stage + nr;
+        __syncthreads();
     }
+    pool_layout(p, recv_v, offs, lane);
+    const int* off_v = offs;
     int run_reg = 0;
     if (kRegRun) {
         run_reg = lane < p.El ? base[lane] : 0;
     } else {
         for (int le = lane; le < p.El; le += 64) run[le] = base[le];
     }
-    if (staged || !kRegRun) __syncthreads();
+    __syncthreads();
+    if (c == 0 && s == 0) pool_publish(p, recv_v, offs, lane);
     // padding rows of the experts this work-group owns (le = its index, then every chunks*S further):
     // metadata and scatter target all ones
     const size_t cap_rows = (size_t)p.max_blocks * p.BM;
@@ -298,9 +313,6 @@ hipError_t launch_route(const Params& p, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_scan_kernel, dim3(p.S), dim3(1024), 0, stream, p);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_pool_kernel, dim3(1), dim3(1024), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (p.El <= 64) hipLaunchKernelGGL(route_table_kernel<true>, grid, dim3(64), 0, stream, p);
