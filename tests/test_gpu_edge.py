@@ -351,3 +351,30 @@ def test_forced_timeout_latches_status_and_recovers():
     assert run.status == 0
     _whole(run, inputs_np(run))
     run.close()
+
+
+@pytest.mark.parametrize("case", ["max_hidden", "max_intermediate", "max_topk", "max_shards"])
+def test_maximum_sizes_whole_layer(case):
+    """The configuration maxima: H = 16384 (128 K steps in GEMM1, 16 fill and 32 combine chunks per
+    lane), I = 16384 (128 K steps in GEMM2, 64 GEMM1 n tiles), K = 64 (every lane of the combine's
+    ballot is a top-k slot, 64 local experts), and S = 64 shards through the whole layer."""
+    print(f"[case] maximum sizes {case}", flush=True)
+    if case == "max_hidden":
+        sh = MoEShape("maxh", 2, 24, 16384, 4096, 2, 1, 1, 64, seed=81)
+        tps = [24, 19]
+    elif case == "max_intermediate":
+        sh = MoEShape("maxi", 2, 24, 4096, 16384, 2, 1, 1, 64, seed=84)
+        tps = [24, 11]
+    elif case == "max_topk":
+        sh = MoEShape("maxk", 2, 30, 256, 128, 128, 64, 64, 64, local_rank=1, seed=82)
+        tps = [30, 23]
+    else:
+        sh = MoEShape("maxs", 64, 12, 256, 128, 16, 8, 2, 64, local_rank=1, seed=83)
+        tps = [(5 * i) % 13 for i in range(64)]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    run = Run(sh, inputs=inp)
+    assert run.status == 0
+    n = inputs_np(run)
+    check_layout(run, n)
+    _whole(run, n)
+    run.close()
