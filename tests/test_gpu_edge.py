@@ -378,3 +378,33 @@ def test_maximum_sizes_whole_layer(case):
     check_layout(run, n)
     _whole(run, n)
     run.close()
+
+
+def test_two_handles_on_two_streams():
+    """Two handles with their own workspaces run interleaved forwards on two streams (default
+    priority) at once; each result equals the same handle's forward run alone (the library keeps no
+    state outside a handle's workspace)."""
+    print("[case] two handles, two streams", flush=True)
+    sa = MoEShape("sa", 3, 120, 512, 256, 32, 8, 4, 64, local_rank=2, seed=91)
+    sb = MoEShape("sb", 2, 200, 768, 384, 16, 4, 2, 128, local_rank=1, seed=92)
+    a = on_gpu(make_inputs(sa, tokens_per_shard=[120, 77, 5]))
+    b = on_gpu(make_inputs(sb, tokens_per_shard=[200, 131]))
+    ma, mb = mm.MegaMoE.from_shape(sa), mm.MegaMoE.from_shape(sb)
+    ya, yb = ma(a), mb(b)                     # alone, on the current stream (also packs the weights)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a, outs_b = [], []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            outs_a.append(ma(a, stream=s1))
+        with torch.cuda.stream(s2):
+            outs_b.append(mb(b, stream=s2))
+    torch.cuda.synchronize()
+
+    def same(u, v, tps):
+        return all(torch.equal(u[i, :n].view(torch.int16), v[i, :n].view(torch.int16)) for i, n in enumerate(tps))
+    assert all(same(o, ya, a["tokens_per_shard"]) for o in outs_a)
+    assert all(same(o, yb, b["tokens_per_shard"]) for o in outs_b)
+    assert ma.status() == 0 and mb.status() == 0
+    ma.close()
+    mb.close()
