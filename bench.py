@@ -111,11 +111,18 @@ def main():
         n = args.calibrate_copy * 2 ** 20 // 4
         src = torch.randint(0, 2 ** 30, (n,), dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        t0.record()
         for _ in range(5):
             torch.bitwise_not(src, out=dst)
+        t1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5,
-                          "kernel": "torch.bitwise_not (elementwise int32)"}))
+        ms = t0.elapsed_time(t1) / 5
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 6,
+                          "kernel": "torch.bitwise_not (elementwise int32)", "ms_per_copy": ms,
+                          "copy_GB/s": 2 * n * 4 / (ms * 1e-3) / 1e9}))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's expert-parallel share; --gpus {args.gpus} is not supported "
