@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-m", type=int, default=None, choices=(64, 128),
+                    help="override the workload's BLOCK_M")
     ap.add_argument("--shared-experts", type=int, default=0, choices=(0, 1),
                     help="add a shared expert on the own shard's tokens (pool segment + combine slot K)")
     ap.add_argument("--graph", action="store_true",
@@ -136,6 +138,8 @@ def main():
     shape = SHAPES[args.workload]
     if args.shared_experts:
         shape = shape.replace(num_shared_experts=args.shared_experts)
+    if args.block_m:
+        shape = shape.replace(block_m=args.block_m)
     torch.cuda.set_device(0)
     inp = make_inputs(shape, device="cuda")
     moe = mm.MegaMoE.from_shape(shape, flags=mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0)

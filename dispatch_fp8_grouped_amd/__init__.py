@@ -33,6 +33,7 @@ STATUS_TIMEOUT = 0x8
 FLAG_KEEP_GEMM1_OUTPUT = 0x1
 FLAG_FILL_IN_GEMM1 = 0x2
 FLAG_DEBUG_FORCE_TIMEOUT = 0x4
+FLAG_DEBUG_POISON = 0x8
 
 STAGE_ROUTE = 0x1
 STAGE_FILL = 0x2

@@ -56,7 +56,7 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->topk < 1 || c->topk > MEGA_MOE_MAX_TOPK) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->block_m != 0 && c->block_m != 64 && c->block_m != 128) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->flags & ~(MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT | MEGA_MOE_FLAG_FILL_IN_GEMM1 |
-                     MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT)) return MEGA_MOE_ERR_UNSUPPORTED;
+                     MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT | MEGA_MOE_FLAG_DEBUG_POISON)) return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
     // the shared expert reads the own shard and takes combine slot K (a lane of the combine's ballot)
@@ -300,6 +300,16 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
     auto mark = [&](int i) {
         if (h->timing && !rc && hipEventRecord(h->ev[set][i], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
     };
+    if (!rc && route && (c.flags & MEGA_MOE_FLAG_DEBUG_POISON)) {
+        // every region a stage fills for a later one: a read of anything this forward did not write
+        // shows up as NaN in the output
+        const uint64_t regions[][2] = {{L.pool_x, L.pool_sf}, {L.pool_sf, L.pool_meta}, {L.l2_x, L.l2_sf},
+                                       {L.l2_sf, L.comb}};
+        for (const auto& r : regions)
+            if (!rc && hipMemsetAsync(w + r[0], 0xFF, r[1] - r[0], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+        const uint64_t comb_end = L.gemm1_out ? L.gemm1_out : L.sched;
+        if (!rc && hipMemsetAsync(w + L.comb, 0xFF, comb_end - L.comb, st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+    }
     mark(0);
     for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i) {
         if (on[i] && !rc) {

@@ -72,6 +72,11 @@ extern "C" {
                                                   once and latches MEGA_MOE_STATUS_TIMEOUT (the kernel
                                                   still exits normally and zeroes its schedule words; the
                                                   output is undefined) */
+#define MEGA_MOE_FLAG_DEBUG_POISON 0x8u        /* tests: before each forward, fill the pool, its scales, the
+                                                  L2 pool, its scales and the combine buffer with 0xFF bytes
+                                                  (NaN as e4m3fn, fp32 and bf16), so any value read before
+                                                  this forward wrote it turns the output into NaN (uses
+                                                  hipMemsetAsync: not for graph capture) */
 
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
 #define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */

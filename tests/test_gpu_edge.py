@@ -408,3 +408,33 @@ def test_two_handles_on_two_streams():
     assert ma.status() == 0 and mb.status() == 0
     ma.close()
     mb.close()
+
+
+@pytest.mark.parametrize("case", ["bm64_shared", "bm128_fill_in_gemm1"])
+def test_poisoned_workspace_gives_identical_output(case):
+    """With the pool, the L2 pool and the combine planes filled with NaN bytes before every forward,
+    the output is bit-identical to a clean run: no stage reads a value this forward did not write.
+    With the arrival-counted schedule this also shows that no GEMM1 load overtakes the fill."""
+    print(f"[case] poisoned workspace {case}", flush=True)
+    if case == "bm64_shared":
+        sh = MoEShape("poison64", 3, 140, 512, 256, 32, 8, 4, 64, local_rank=1, num_shared_experts=1, seed=95)
+        tps, flags = [140, 61, 0], 0
+    else:
+        sh = MoEShape("poison128", 4, 300, 1024, 512, 32, 8, 8, 128, local_rank=3, routing="zipf", seed=96)
+        tps, flags = [300, 17, 299, 150], mm.FLAG_FILL_IN_GEMM1
+    inp = make_inputs(sh, tokens_per_shard=tps)
+    clean = Run(sh, inputs=inp, flags=flags)
+    pois = Run(sh, inputs=inp, flags=flags | mm.FLAG_DEBUG_POISON, repeat=2)
+    assert clean.status == 0 and pois.status == 0
+    for y in pois.ys:
+        for i, n in enumerate(tps):
+            assert torch.isfinite(y[i, :n].float()).all()
+            assert torch.equal(y[i, :n].view(torch.int16), clean.y[i, :n].view(torch.int16))
+    _whole(clean, inputs_np(clean))
+    # the poison is really there: a routing-only forward leaves the pool and combine bytes at 0xFF
+    pois.moe(pois.inp_gpu, stages=mm.STAGE_ROUTE)
+    torch.cuda.synchronize()
+    for name in ("pool_x", "l2_x", "comb"):
+        assert (pois.region(name, torch.uint8, (4096,)) == 255).all(), name
+    clean.close()
+    pois.close()
