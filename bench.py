@@ -1,6 +1,6 @@
 """Benchmark of the fused FP8 MoE layer on one MI355X: routed tokens/s and GEMM % of FP8 MFMA peak.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 20] [--workload prefill] [--no-cpu-baseline]
 
 One step = one mega_moe_forward (routing, pool fill, GEMM1 + SwiGLU + requant, GEMM2 + scatter,
 combine) over one resident batch of seeded synthetic inputs.  The timed region brackets exactly
@@ -90,7 +90,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-m", type=int, default=None, choices=(64, 128),
