@@ -438,3 +438,38 @@ def test_poisoned_workspace_gives_identical_output(case):
         assert (pois.region(name, torch.uint8, (4096,)) == 255).all(), name
     clean.close()
     pois.close()
+
+
+@pytest.mark.parametrize("case", ["no_tokens", "all_sentinels", "all_remote"])
+def test_empty_forward(case):
+    """Nothing routed to this GPU: no valid tokens at all (y untouched), valid tokens whose top-k
+    entries are all -1, or whose experts all live on other ranks (y rows zero).  No pool block
+    exists, every GEMM work-group exits at once, and the next forward on the same handle is exact."""
+    print(f"[case] empty forward {case}", flush=True)
+    sh = MoEShape("empty", 3, 64, 256, 128, 32, 8, 4, 64, local_rank=1, seed=97)
+    inp = on_gpu(make_inputs(sh))
+    if case == "no_tokens":
+        inp["tokens_per_shard"] = [0, 0, 0]
+    elif case == "all_sentinels":
+        inp["topk_idx"].fill_(-1)
+    else:
+        inp["topk_idx"].remainder_(8)            # experts 0..7: rank 0's, none of rank 1's
+    moe = mm.MegaMoE.from_shape(sh)
+    y = torch.full((3, 64, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe(inp, y=y)
+    torch.cuda.synchronize()
+    assert moe.status() == 0
+    assert int(moe.region("status", torch.int32, (2,))[1].item()) == 0      # no pool block
+    if case == "no_tokens":
+        assert torch.isnan(y.float()).all()
+    else:
+        assert (y.float() == 0).all()
+    full = on_gpu(make_inputs(sh))
+    full["w1_packed"], full["w2_packed"] = inp["w1_packed"], inp["w2_packed"]
+    y2 = moe(full)
+    torch.cuda.synchronize()
+    assert moe.status() == 0
+    n = to_numpy(full)
+    ref = oracle.forward(n, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m)
+    tol_check(y2.to(torch.float64).cpu().numpy(), ref["y"], case)
+    moe.close()
