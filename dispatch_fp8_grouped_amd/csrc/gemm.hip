@@ -21,11 +21,12 @@
 //
 // Pipeline: a K step's operands (A and B tiles, the token scales, the two weight-block scales and, for
 // GEMM2, the tile's pool metadata) arrive by LDS DMA (global_load_lds) into one of three LDS stages.
-// The persistent work-group walks its (tile, K step) sequence as one stream: step s waits until stage s
-// has landed (vmcnt counts only the one younger stage), barriers, issues the DMA of step s+2 into the
-// stage freed by step s-1, then runs its MFMAs; the next tile's first steps load during the current
-// tile's last ones.  Every step issues the same number of DMA instructions (past the end the last step
-// is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
+// The persistent work-group walks its (tile, K step) sequence as one stream.  Step s computes from
+// registers that were read from LDS during step s-1; half-way through, it waits until stage s+1 has
+// landed (vmcnt lets only the youngest DMA group stay in flight), barriers, refills its own stage with
+// step s+3 and reads stage s+1 into the second register set while its remaining MFMAs run.  The next
+// tile's first steps load during the current tile's last ones.  Every step issues the same number of
+// DMA instructions (past the end the last step is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
 // XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
 // Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of one expert (a few
 // n tiles of all its pool blocks), which share A and B through that XCD's L2.
