@@ -125,6 +125,11 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, const void
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once (the caches keep it at low priority)
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, const void* dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
+}
 // 4 bytes per lane from a per-lane address (every lane active)
 __device__ __forceinline__ void dma4_lane(const void* src, const void* dst) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
@@ -320,8 +325,11 @@ using ic = std::integral_constant<int, V>;
 #endif
 
 // Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.  kFill (GEMM1 only): the work-groups
-// first pull the pool rows (fill_pool) and every tile waits for its block's arrival count.
-template <int BM, int NW, bool kGemm1, bool kFill>
+// first pull the pool rows (fill_pool) and every tile waits for its block's arrival count.  kStreamW:
+// the weight DMA carries the non-temporal hint, for launches where each weight chunk is read by one
+// tile only (about one pool block per expert, as at decode); where several blocks of an expert share a
+// weight chunk through L2 (prefill) the hint costs 11% and is not used.
+template <int BM, int NW, bool kGemm1, bool kFill, bool kStreamW>
 __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int NWN = NW / 2;                 // compute waves along the weight (N) side
     constexpr int TM = BM / 32;                 // 16-token subtiles per wave (wave covers BM/2 tokens)
@@ -467,7 +475,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) dma16(iA, a_off[i], &sA[buf][(i * NW + wave) * 1024]);
 #pragma unroll
-        for (int i = 0; i < B_INS; ++i) dma16(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
+        for (int i = 0; i < B_INS; ++i) {
+            if constexpr (kStreamW) dma16_nt(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
+            else dma16(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
+        }
         dma4_lane(iSm, &sSmall[buf][wave * 64]);
     };
     // advance to the next step; past the last step the last step is loaded again (constant DMA count)
@@ -758,24 +769,32 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     if constexpr (kFill) sched_exit(p, nblocks, tid);
 }
 
-template <int BM, bool kGemm1, bool kFill = false>
+template <int BM, bool kGemm1, bool kFill = false, bool kStreamW = false>
 hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     int grid = (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kFill>), dim3(grid), dim3(kWaves * 64), 0, stream,
-                       p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kFill, kStreamW>), dim3(grid), dim3(kWaves * 64), 0,
+                       stream, p);
     return hipGetLastError();
 }
+
+// Weights stream (each chunk read by one tile) when an expert is expected to fill at most one pool
+// block: S*T_max*K/E routed rows per expert under uniform routing, against BLOCK_M.
+bool weights_stream(const Params& p) { return (double)p.S * p.T_max * p.K / p.E <= (double)p.BM; }
 
 }  // namespace
 
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
     if (fuse_fill)
         return p.BM == 64 ? launch<64, true, true>(p, num_cus, stream) : launch<128, true, true>(p, num_cus, stream);
-    return p.BM == 64 ? launch<64, true>(p, num_cus, stream) : launch<128, true>(p, num_cus, stream);
+    if (p.BM == 64)
+        return weights_stream(p) ? launch<64, true, false, true>(p, num_cus, stream) : launch<64, true>(p, num_cus, stream);
+    return launch<128, true>(p, num_cus, stream);
 }
 
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream) {
-    return p.BM == 64 ? launch<64, false>(p, num_cus, stream) : launch<128, false>(p, num_cus, stream);
+    if (p.BM == 64)
+        return weights_stream(p) ? launch<64, false, false, true>(p, num_cus, stream) : launch<64, false>(p, num_cus, stream);
+    return launch<128, false>(p, num_cus, stream);
 }
 
 }  // namespace mm
