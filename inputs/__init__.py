@@ -49,6 +49,7 @@ class MoEShape:
     local_rank: int = 0
     routing: str = "uniform"   # "uniform" | "zipf"
     num_shared_experts: int = 0  # 0 or 1: a shared expert on shard local_rank's own tokens
+    weight_format: str = "fp8"   # "fp8" (128x128 block scales) | "mxfp4" (e2m1, UE8M0 per 32 along K)
     zipf_alpha: float = 1.2
     seed: int = 0
 
@@ -87,6 +88,29 @@ def _quant_block128(w: torch.Tensor):
     return q.reshape(n, c).view(torch.uint8), scale.to(torch.float32)
 
 
+_E2M1_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _quant_mxfp4(w: torch.Tensor):
+    """[N, C] float32 -> (uint8 [N, C/2] two e2m1 codes per byte, low nibble = lower column;
+    uint8 [N, C/32] UE8M0 exponents).  Per 32 columns: exponent = floor(log2(amax)) - 2 (6 = 1.5 * 2^2 is
+    the largest e2m1 magnitude), clamped to the UE8M0 range; each value goes to the nearest e2m1
+    magnitude of w / 2^exponent, saturating at 6.  This plays the upstream model that hands the layer
+    MXFP4 weights."""
+    n, c = w.shape
+    wb = w.reshape(n, c // 32, 32)
+    amax = wb.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(2.0 ** -126))) - 2,
+                    torch.full_like(amax, -127.0)).clamp(-127, 127)
+    v = (wb / torch.pow(2.0, e).unsqueeze(-1)).abs().clamp(max=6.0)
+    mags = torch.tensor(_E2M1_MAGS, device=w.device)
+    code = (v.unsqueeze(-1) - mags).abs().argmin(dim=-1).to(torch.uint8)
+    code = code | torch.where(wb < 0, 8, 0).to(torch.uint8)
+    code = code.reshape(n, c)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).to(torch.uint8)
+    return packed, (e + 127).to(torch.uint8).reshape(n, c // 32)
+
+
 def _route(shape: MoEShape, gen: torch.Generator, device) -> torch.Tensor:
     S, T, E, K = shape.num_shards, shape.max_tokens_per_shard, shape.num_experts, shape.topk
     if shape.routing == "uniform":
@@ -114,6 +138,9 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
     w2 [E_w,H,I] u8, w2_sf [E_w,H/128,I/128] f32 (E_w = E_l + num_shared_experts), and
     tokens_per_shard (list of int).
 
+    weight_format "mxfp4": w1 [E_w,2I,H/2] and w2 [E_w,H,I/2] hold two e2m1 codes per byte, and w1_sf
+    [E_w,2I,H/32] / w2_sf [E_w,H,I/32] hold UE8M0 exponents (uint8) of each 32 values along K.
+
     integer_codes=True draws every FP8 code from the integers -8..8 and every scale as
     one shared power of two (2^-4 for activations, 2^-6 for weights), so that every
     product and every partial sum of the GEMMs is exact in fp32.
@@ -136,6 +163,18 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
         w1_sf = torch.full((El, 2 * I // 128, H // 128), 2.0 ** -6, device=device)
         w2 = ints((El, H, I))
         w2_sf = torch.full((El, H // 128, I // 128), 2.0 ** -6, device=device)
+    elif shape.weight_format == "mxfp4":
+        x, x_sf = _quant_rows_per128(torch.randn((S, T, H), generator=gen, device=device))
+        w1 = torch.empty((El, 2 * I, H // 2), dtype=torch.uint8, device=device)
+        w1_sf = torch.empty((El, 2 * I, H // 32), dtype=torch.uint8, device=device)
+        for e in range(El):
+            w = torch.randn((2 * I, H), generator=gen, device=device) * 0.02
+            w1[e], w1_sf[e] = _quant_mxfp4(w)
+        w2 = torch.empty((El, H, I // 2), dtype=torch.uint8, device=device)
+        w2_sf = torch.empty((El, H, I // 32), dtype=torch.uint8, device=device)
+        for e in range(El):
+            w = torch.randn((H, I), generator=gen, device=device) * 0.02
+            w2[e], w2_sf[e] = _quant_mxfp4(w)
     else:
         x, x_sf = _quant_rows_per128(torch.randn((S, T, H), generator=gen, device=device))
         w1 = torch.empty((El, 2 * I, H), dtype=torch.uint8, device=device)

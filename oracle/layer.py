@@ -13,6 +13,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
+from .fp4 import dequant_mx
 from .fp8 import e4m3fn_decode, e4m3fn_encode, bf16_round, E4M3_MAX
 
 META_PAD = 0xFFFFFFFF
@@ -249,6 +250,14 @@ def requant_rows(h: np.ndarray, gran: int = 128):
     return codes, s
 
 
+def dequant_weight(codes: np.ndarray, sf: np.ndarray) -> np.ndarray:
+    """One expert's weight in either format: FP8 codes [N, C] with fp32 128x128 block scales, or MXFP4
+    (packed e2m1 [N, C/2] with UE8M0 bytes [N, C/32]; oracle/fp4.py), told apart by the scale dtype."""
+    if np.asarray(sf).dtype == np.uint8:
+        return dequant_mx(codes, sf)
+    return dequant_blocks(codes, sf)
+
+
 def expert_ffn_rows(a_codes, a_sf, w1_codes, w1_sf, w2_codes, w2_sf, intermediate: int,
                     gran: int = 128, return_parts: bool = False):
     """One expert's FFN on pooled rows: GEMM1 -> SwiGLU -> FP8 requant -> GEMM2 -> bf16.
@@ -260,12 +269,12 @@ def expert_ffn_rows(a_codes, a_sf, w1_codes, w1_sf, w2_codes, w2_sf, intermediat
     analysis", 8.1-8.2).
     """
     a = dequant_rows(a_codes, a_sf)
-    w1 = dequant_blocks(w1_codes, w1_sf)
+    w1 = dequant_weight(w1_codes, w1_sf)
     g = a @ w1.T
     h = swiglu(g, intermediate)
     q, s = requant_rows(h, gran)
     hq = dequant_rows_gran(q, s, gran)
-    w2 = dequant_blocks(w2_codes, w2_sf)
+    w2 = dequant_weight(w2_codes, w2_sf)
     o = bf16_round(hq @ w2.T)
     if return_parts:
         return o, dict(g=g, h=h, l2_codes=q, l2_sf=s)
@@ -313,7 +322,7 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
     tps = inp["tokens_per_shard"]
     S, T_max, K = idx.shape
     H = x.shape[2]
-    I = inp["w2"].shape[2]
+    I = inp["w2_sf"].shape[2] * (32 if inp["w2_sf"].dtype == np.uint8 else 128)
     rt = route(idx, tps, num_experts, num_local_experts, local_rank)
     shared = num_shared_experts > 0
     pool_x, pool_sf, pool_meta, off = fill_pool(x, x_sf, rt, block_m, K,
@@ -369,7 +378,7 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
     """
     K = inp["topk_idx"].shape[2]
     lo = local_rank * num_local_experts
-    I = inp["w2"].shape[2]
+    I = inp["w2_sf"].shape[2] * (32 if inp["w2_sf"].dtype == np.uint8 else 128)
     a_codes = inp["x"][s, t][None, :]
     a_sf = inp["x_sf"][s, t][None, :]
     acc = np.zeros(inp["x"].shape[2], dtype=np.float64)
@@ -386,8 +395,8 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
                                 inp["w2_sf"][le], I, gran)[0]
         else:
             if le not in cache:
-                cache[le] = (dequant_blocks(inp["w1"][le], inp["w1_sf"][le]),
-                             dequant_blocks(inp["w2"][le], inp["w2_sf"][le]))
+                cache[le] = (dequant_weight(inp["w1"][le], inp["w1_sf"][le]),
+                             dequant_weight(inp["w2"][le], inp["w2_sf"][le]))
             o = ffn_dequantised(dequant_rows(a_codes, a_sf), cache[le][0], cache[le][1], I, gran)[0]
         acc += wk * o
     return bf16_round(acc)
