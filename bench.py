@@ -48,7 +48,8 @@ def algorithmic(shape, R, N, shared_rows=0):
         fill_bytes=R * (2 * H + 2 * (H // 128) * 4 + 12 + 4),
         # combine: read each routed pair's bf16 row, read K ids + weights per token, write the bf16 row
         combine_bytes=R * 2 * H + N * (2 * H + K * 12),
-        weight_bytes=El * 3 * H * I + El * (2 * I // 128) * (H // 128) * 4 + El * (H // 128) * (I // 128) * 4,
+        weight_bytes=(El * 3 * H * I // 2 + El * 3 * H * I // 32) if shape.weight_format == "mxfp4" else
+                     El * 3 * H * I + El * (2 * I // 128) * (H // 128) * 4 + El * (H // 128) * (I // 128) * 4,
     )
 
 
@@ -95,6 +96,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-m", type=int, default=None, choices=(64, 128),
                     help="override the workload's BLOCK_M")
+    ap.add_argument("--weight-format", default="fp8", choices=("fp8", "mxfp4"),
+                    help="expert weights: FP8 with 128x128 block scales (the workloads' format) or MXFP4 "
+                         "(e2m1 with UE8M0 exponents per 32 K; the FP8 x FP4 variant)")
     ap.add_argument("--shared-experts", type=int, default=0, choices=(0, 1),
                     help="add a shared expert on the own shard's tokens (pool segment + combine slot K)")
     ap.add_argument("--graph", action="store_true",
@@ -140,6 +144,8 @@ def main():
         shape = shape.replace(num_shared_experts=args.shared_experts)
     if args.block_m:
         shape = shape.replace(block_m=args.block_m)
+    if args.weight_format != "fp8":
+        shape = shape.replace(weight_format=args.weight_format)
     torch.cuda.set_device(0)
     inp = make_inputs(shape, device="cuda")
     moe = mm.MegaMoE.from_shape(shape, flags=mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0)
@@ -218,9 +224,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": "fp8 x fp4" if shape.weight_format == "mxfp4" else "fp8",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload] + (
+                       ", weights MXFP4 (e2m1, UE8M0 per 32 K)" if shape.weight_format == "mxfp4" else "") + (
                        f", plus a shared expert on shard {shape.local_rank}'s {shared_rows} tokens"
                        if shape.num_shared_experts else ""), "routed_rows": R, "tokens": N,
                    "parallelism": "one GPU's EP share, source ranks emulated as shards"},

@@ -35,6 +35,9 @@ FLAG_FILL_IN_GEMM1 = 0x2
 FLAG_DEBUG_FORCE_TIMEOUT = 0x4
 FLAG_DEBUG_POISON = 0x8
 
+WEIGHTS_FP8 = 0
+WEIGHTS_MXFP4 = 1
+
 STAGE_ROUTE = 0x1
 STAGE_FILL = 0x2
 STAGE_GEMM1 = 0x4
@@ -62,7 +65,8 @@ class mega_moe_config(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("num_local_experts", ctypes.c_int32),
                 ("local_rank", ctypes.c_int32), ("topk", ctypes.c_int32), ("block_m", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("num_shared_experts", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("num_shared_experts", ctypes.c_int32),
+                ("weight_format", ctypes.c_int32)]
 
 
 _LAYOUT_U64 = ("status", "chunk_hist", "chunk_base", "send", "recv", "recv_tot", "pool_off", "block_expert",
@@ -137,9 +141,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(num_shards, max_tokens_per_shard, hidden, intermediate, num_experts, num_local_experts,
-                topk, block_m=0, local_rank=0, flags=0, num_shared_experts=0) -> mega_moe_config:
+                topk, block_m=0, local_rank=0, flags=0, num_shared_experts=0,
+                weight_format=WEIGHTS_FP8) -> mega_moe_config:
     return mega_moe_config(num_shards, max_tokens_per_shard, hidden, intermediate, num_experts,
-                           num_local_experts, local_rank, topk, block_m, flags, num_shared_experts)
+                           num_local_experts, local_rank, topk, block_m, flags, num_shared_experts, weight_format)
 
 
 # --------------------------------------------------------------- the C entry points, same names
@@ -222,10 +227,11 @@ class MegaMoE:
     """Owns a workspace tensor and a handle; checks tensor shapes and dtypes before each call."""
 
     def __init__(self, num_shards, max_tokens_per_shard, hidden, intermediate, num_experts, num_local_experts,
-                 topk, block_m=0, local_rank=0, flags=0, num_shared_experts=0, device="cuda", stream=None):
+                 topk, block_m=0, local_rank=0, flags=0, num_shared_experts=0, weight_format=WEIGHTS_FP8,
+                 device="cuda", stream=None):
         import torch
         self.cfg = make_config(num_shards, max_tokens_per_shard, hidden, intermediate, num_experts,
-                               num_local_experts, topk, block_m, local_rank, flags, num_shared_experts)
+                               num_local_experts, topk, block_m, local_rank, flags, num_shared_experts, weight_format)
         self.nbytes = mega_moe_workspace_bytes(self.cfg)
         self.workspace = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         self.h = mega_moe_init(self.cfg, self.workspace, self.nbytes, stream)
@@ -236,7 +242,8 @@ class MegaMoE:
     def from_shape(cls, shape, flags=0, **kw):
         return cls(shape.num_shards, shape.max_tokens_per_shard, shape.hidden, shape.intermediate,
                    shape.num_experts, shape.num_local_experts, shape.topk, shape.block_m, shape.local_rank,
-                   flags, getattr(shape, "num_shared_experts", 0), **kw)
+                   flags, getattr(shape, "num_shared_experts", 0),
+                   WEIGHTS_MXFP4 if getattr(shape, "weight_format", "fp8") == "mxfp4" else WEIGHTS_FP8, **kw)
 
     def close(self):
         if self.h is not None:
@@ -258,10 +265,13 @@ class MegaMoE:
                 ("topk_idx", topk_idx, (S, T, K), torch.int64),
                 ("topk_weights", topk_weights, (S, T, K), torch.float32),
                 ("w1 (packed)", w1, self.packed_shapes()[0], torch.uint8),
-                ("w1_sf", w1_sf, (El, 2 * I // 128, H // 128), torch.float32),
-                ("w2 (packed)", w2, self.packed_shapes()[1], torch.uint8),
-                ("w2_sf", w2_sf, (El, H // 128, I // 128), torch.float32),
-                ("y", y, (S, T, H), torch.bfloat16)]
+                ("w2 (packed)", w2, self.packed_shapes()[1], torch.uint8)]
+        if c.weight_format == WEIGHTS_MXFP4:
+            want += [("w1_sf", w1_sf, (El, 2 * I, H // 32), torch.uint8), ("w2_sf", w2_sf, (El, H, I // 32), torch.uint8)]
+        else:
+            want += [("w1_sf", w1_sf, (El, 2 * I // 128, H // 128), torch.float32),
+                     ("w2_sf", w2_sf, (El, H // 128, I // 128), torch.float32)]
+        want += [("y", y, (S, T, H), torch.bfloat16)]
         for name, t, shape, dtype in want:
             if t is None:
                 continue
@@ -273,7 +283,8 @@ class MegaMoE:
         """Shapes of the packed W1 and W2 (see mega_moe_pack_weights)."""
         c = self.cfg
         El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
-        return (El, I // 128, H // 128, 256, 128), (El, H // 256, I // 128, 256, 128)
+        rb = 64 if c.weight_format == WEIGHTS_MXFP4 else 128     # bytes per row and 128-value K step
+        return (El, I // 128, H // 128, 256, rb), (El, H // 256, I // 128, 256, rb)
 
     def pack_weights(self, w1, w2, stream=None):
         """Row-major W1 [E_w,2I,H] and W2 [E_w,H,I] (uint8 e4m3fn; E_w = E_l + shared experts, the shared
@@ -281,7 +292,8 @@ class MegaMoE:
         import torch
         c = self.cfg
         El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
-        for name, t, shape in (("w1", w1, (El, 2 * I, H)), ("w2", w2, (El, H, I))):
+        d = 2 if c.weight_format == WEIGHTS_MXFP4 else 1          # two e2m1 codes per byte
+        for name, t, shape in (("w1", w1, (El, 2 * I, H // d)), ("w2", w2, (El, H, I // d))):
             if tuple(t.shape) != shape or t.dtype != torch.uint8 or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"{name}: want contiguous cuda uint8 {shape}, got {t.dtype} {tuple(t.shape)}")
         s1, s2 = self.packed_shapes()

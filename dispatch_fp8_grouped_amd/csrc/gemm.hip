@@ -46,6 +46,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
 constexpr int kStages = 3;
 
+// MXFP4 weight fragment (16 rows x 128 K as e2m1, 16 bytes per lane) times an FP8 token fragment; the
+// weight rows' UE8M0 exponents come in through the MFMA's A-scale operand (byte 0 of `sa`, one per lane:
+// its row and its 32-value K block), the token side is unscaled (127 = 2^0).
+__device__ __forceinline__ v4f mfma_fp4w(const v4i& a, const v8i& b, uint32_t sa, const v4f& c) {
+    const v8i aw = __builtin_shufflevector(a, v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, b, c, 4, 0, 0, (int)sa, 0, 127);
+}
+
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // scale operands 0 select the unscaled v_mfma_f32_16x16x128_f8f6f4; format 0 = FP8 e4m3
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -55,6 +63,9 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
 // of one fragment read land in 16 different 16-byte bank slots whether the LDS serves 8 or 16 lanes of a
 // 128-bit read per cycle.
 __device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+// 64-byte rows (MXFP4 weights, four 16-byte chunks): chunk c of row r at c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1),
+// so the 16 rows of a fragment read land in distinct 16-byte bank slots for 8- and 16-lane LDS cycles.
+__device__ __forceinline__ int swz4_chunk(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + (swz_chunk(r, c) << 4); }
 
 // Fragment of 16 rows x 128 K bytes for one MFMA operand: lane l takes row (l & 15) and the 32 bytes
@@ -328,8 +339,9 @@ using ic = std::integral_constant<int, V>;
 // first pull the pool rows (fill_pool) and every tile waits for its block's arrival count.  kStreamW:
 // the weight DMA carries the non-temporal hint, for launches where each weight chunk is read by one
 // tile only (about one pool block per expert, as at decode); where several blocks of an expert share a
-// weight chunk through L2 (prefill) the hint costs 11% and is not used.
-template <int BM, int NW, bool kGemm1, bool kFill, bool kStreamW>
+// weight chunk through L2 (prefill) the hint costs 11% and is not used.  kFp4: MXFP4 weights (two e2m1
+// codes per byte, 64-byte rows per K step, UE8M0 exponents per 32 K applied by the MFMA's scale operand).
+template <int BM, int NW, bool kGemm1, bool kFill, bool kStreamW, bool kFp4>
 __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int NWN = NW / 2;                 // compute waves along the weight (N) side
     constexpr int TM = BM / 32;                 // 16-token subtiles per wave (wave covers BM/2 tokens)
@@ -338,9 +350,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int HC = WROWS / 2;               // GEMM1: output columns per wave (gate + up halves)
     constexpr int NMF = TM * WN;                // MFMAs per wave and K step
     constexpr int A_INS = BM / (8 * NW);        // 1 KB A DMA instructions per wave and step
-    constexpr int B_INS = 32 / NW;              // 1 KB B DMA instructions per wave and step
+    constexpr int WRB = kFp4 ? 64 : 128;       // weight bytes per row and K step
+    constexpr int B_INS = (256 * WRB / 1024) / NW;   // 1 KB B DMA instructions per wave and step
     constexpr int SA_LANES = BM / NW;           // token rows whose scale (and GEMM2 target) a wave loads
-    constexpr int DMA_PER_STEP = A_INS + B_INS + 1;
+    // per step: A and B chunks, the small DMA and (MXFP4) the wave's weight-row exponents
+    constexpr int DMA_PER_STEP = A_INS + B_INS + 1 + (kFp4 ? 1 : 0);
     // global stores every wave issues in a GEMM2 tile's epilogue: two per 16-token group
     constexpr int kEpiStores = 2 * TM;
     // K-start rotation per block within the expert and per n tile (see the issue side below); it
@@ -352,7 +366,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     static_assert(kGemm1 || !kFill, "the fill feeds GEMM1 only");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * WRB];
+    // MXFP4: per stage and wave, the UE8M0 exponents of the wave's 64 weight rows (4 bytes = 4 K blocks)
+    __shared__ __attribute__((aligned(16))) uint32_t sWs[kStages][kFp4 ? NW * 64 : 1];
     // per stage and wave, 64 dwords written by one DMA: [0, SA_LANES) token scales of rows
     // wave*SA_LANES + l, then the wave's two weight-block scales, then (GEMM2) the rows' scatter targets
     __shared__ __attribute__((aligned(16))) uint32_t sSmall[kStages][NW * 64];
@@ -413,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // w_base(le, nt) + kb*256*128 (for GEMM1 its rows are the 128 gate rows, then the 128 up rows)
     auto a_base = [&](int b) { return (kGemm1 ? p.pool_x : p.l2_x) + (size_t)b * KB * BM * 128; };
     auto w_base = [&](int le, int nt) {
-        return (kGemm1 ? p.w1 : p.w2) + ((size_t)le * NT + nt) * KB * (256 * 128);
+        return (kGemm1 ? p.w1 : p.w2) + ((size_t)le * NT + nt) * KB * (256 * WRB);
     };
 
     // per-lane DMA offsets (fixed for the whole kernel)
@@ -427,11 +443,18 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
-        b_off[i] = r * 128 + c * 16;
+        if constexpr (kFp4) {
+            const int r4 = (i * NW + wave) * 16 + (lane >> 2), c4 = swz4_chunk(r4, lane & 3);
+            b_off[i] = r4 * 64 + c4 * 16;
+        } else {
+            b_off[i] = r * 128 + c * 16;
+        }
     }
     // lane role in the small DMA: token scale of row wave*SA_LANES + l, weight-block scale j, or
     // (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes repeat lane 0's load
-    const int sm_role = lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? 1 : (!kGemm1 && lane < 2 * SA_LANES + 2) ? 2 : 3;
+    // (MXFP4 weights carry no 128x128 block scales: those two lanes repeat lane 0's load)
+    const int sm_role = lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? (kFp4 ? 3 : 1)
+                      : (!kGemm1 && lane < 2 * SA_LANES + 2) ? 2 : 3;
     const int sm_row = wave * SA_LANES + (sm_role == 0 ? lane : sm_role == 2 ? lane - SA_LANES - 2 : 0);
     // bytes per K step: token scales are block-major (BM per K block), weight scales K-contiguous
     const uint32_t sm_inc = sm_role == 2 ? 0u : sm_role == 1 ? 4u : (uint32_t)(BM * 4);
@@ -445,6 +468,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const uint8_t* iA;
     const uint8_t* iW;
     const uint8_t* iSm;     // per lane
+    const uint8_t* iWs;     // per lane (MXFP4): the exponent bytes of this lane's weight row
+    // MXFP4: the tile row whose exponents this lane loads, fragment lane >> 4, row lane & 15 (the rows
+    // the wave's weight fragments cover, in the order they are read back)
+    const int ws_tr = kGemm1 ? wn * 32 + ((lane >> 4) < 2 ? 0 : 128) + ((lane >> 4) & 1) * 16 + (lane & 15)
+                             : wn * WROWS + (lane >> 4) * 16 + (lane & 15);
     auto set_issue_tile = [&]() __attribute__((always_inline)) {
         int b, nt, le;
         tile_of(ij, b, nt, le);
@@ -456,7 +484,13 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             ikc = kc;
         }
         iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b) + (size_t)ikc * BM * 128));
-        iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt) + (size_t)ikc * 256 * 128));
+        iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt) + (size_t)ikc * 256 * WRB));
+        if constexpr (kFp4) {
+            const int grow = kGemm1 ? (ws_tr < 128 ? nt * 128 + ws_tr : p.I + nt * 128 + ws_tr - 128) : nt * 256 + ws_tr;
+            const size_t nrows = kGemm1 ? (size_t)2 * p.I : (size_t)p.H;
+            iWs = reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf : p.w2_sf) +
+                  ((size_t)le * nrows + grow) * (size_t)(Kdim >> 5) + (size_t)ikc * 4;
+        }
         const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (size_t)b * KB * BM + sm_row;
         int blk;
         if (kGemm1) blk = lane == SA_LANES ? nt : (p.I >> 7) + nt;     // gate block, up block
@@ -480,6 +514,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             else dma16(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
         }
         dma4_lane(iSm, &sSmall[buf][wave * 64]);
+        if constexpr (kFp4) dma4_lane(iWs, &sWs[buf][wave * 64]);
     };
     // advance to the next step; past the last step the last step is loaded again (constant DMA count)
     auto issue_advance = [&]() __attribute__((always_inline)) {
@@ -487,13 +522,15 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             ++ikb;
             if (!kRotate || ++ikc < KB) {
                 iA += BM * 128;
-                iW += 256 * 128;
+                iW += 256 * WRB;
                 iSm += sm_inc;
+                if constexpr (kFp4) iWs += 4;
             } else {                                    // wrap to K block 0
                 ikc = 0;
                 iA -= (size_t)(KB - 1) * BM * 128;
-                iW -= (size_t)(KB - 1) * 256 * 128;
+                iW -= (size_t)(KB - 1) * 256 * WRB;
                 iSm -= (size_t)(KB - 1) * sm_inc;
+                if constexpr (kFp4) iWs -= (size_t)(KB - 1) * 4;
             }
         } else if (ij + 1 < my_tiles) {
             ikb = 0;
@@ -508,10 +545,18 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     auto wrow = [](int a) { return kGemm1 ? (a < WN / 2 ? 0 : 128) + (a % (WN / 2)) * 16 : a * 16; };
     const int xr = wm * (BM / 2) + rr;
     const int wr = (kGemm1 ? wn * HC : wn * WROWS) + rr;
-    const uint8_t* xlo = &sA[0][0] + swz(xr, 2 * g);
-    const uint8_t* xhi = &sA[0][0] + swz(xr, 2 * g + 1);
-    const uint8_t* wlo = &sB[0][0] + swz(wr, 2 * g);
-    const uint8_t* whi = &sB[0][0] + swz(wr, 2 * g + 1);
+    // The f8f6f4 MFMA splits an FP8 operand's K between the lane's two halves: lane group g holds
+    // K 16g..16g+15 in its first 16 bytes and 64+16g..64+16g+15 in its second.  Two FP8 operands loaded
+    // alike only need to agree with each other, so the FP8 path hands group g the contiguous K
+    // 32g..32g+31.  An FP4 operand holds the contiguous K 32g..32g+31 in its 16 bytes (checked on the
+    // chip), so against MXFP4 weights the token fragment must follow the hardware order: chunks g and
+    // g + 4.
+    const uint8_t* xlo = &sA[0][0] + swz(xr, kFp4 ? g : 2 * g);
+    const uint8_t* xhi = &sA[0][0] + swz(xr, kFp4 ? g + 4 : 2 * g + 1);
+    const uint8_t* wlo = &sB[0][0] + (kFp4 ? 0 : swz(wr, 2 * g));
+    const uint8_t* whi = &sB[0][0] + (kFp4 ? 0 : swz(wr, 2 * g + 1));
+    // MXFP4: 16 bytes per lane and fragment, chunk g of the lane's 64-byte row
+    const uint8_t* wq = &sB[0][0] + wr * 64 + swz4_chunk(wr, g) * 16;
 
     // One K step's operands in registers: token and weight fragments, the promotion factors (token
     // scale x weight-block scale; GEMM1 has a gate and an up block) and, for GEMM2, the scatter target
@@ -520,14 +565,16 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int NSW = kGemm1 ? 2 : 1;
     struct Frags {
         v8i x[TM];
-        v8i w[WN];
+        std::conditional_t<kFp4, v4i, v8i> w[WN];
+        uint32_t ws[kFp4 ? WN : 1];   // MXFP4: UE8M0 exponent of the lane's row and K block, per fragment
         float sc[NSW][TM];
         uint32_t dst[kGemm1 ? 1 : TM];
     };
     auto load_head = [&](Frags& f, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
-        const float sw0 = __uint_as_float(sSmall[buf][wave * 64 + SA_LANES]);
-        const float sw1 = __uint_as_float(sSmall[buf][wave * 64 + SA_LANES + 1]);
+        // (MXFP4: the weight scales are applied inside the MFMA)
+        const float sw0 = kFp4 ? 1.0f : __uint_as_float(sSmall[buf][wave * 64 + SA_LANES]);
+        const float sw1 = kFp4 ? 1.0f : __uint_as_float(sSmall[buf][wave * 64 + SA_LANES + 1]);
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const int r = wm * (BM / 2) + t * 16 + rr;          // token row; loaded by wave r / SA_LANES
@@ -540,12 +587,22 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) f.x[t] = load_frag(xlo, xhi, buf * BM * 128 + t * 16 * 128);
 #pragma unroll
-        for (int a = 0; a < WN / 2; ++a) f.w[a] = load_frag(wlo, whi, buf * 256 * 128 + wrow(a) * 128);
+        for (int a = 0; a < WN / 2; ++a) {
+            if constexpr (kFp4) f.w[a] = *reinterpret_cast<const v4i*>(wq + buf * 256 * 64 + wrow(a) * 64);
+            else f.w[a] = load_frag(wlo, whi, buf * 256 * 128 + wrow(a) * 128);
+        }
+        if constexpr (kFp4) {
+#pragma unroll
+            for (int a = 0; a < WN; ++a) f.ws[a] = (sWs[buf][wave * 64 + a * 16 + rr] >> (8 * g)) & 0xFFu;
+        }
     };
     auto load_tail = [&](Frags& f, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-        for (int a = WN / 2; a < WN; ++a) f.w[a] = load_frag(wlo, whi, buf * 256 * 128 + wrow(a) * 128);
+        for (int a = WN / 2; a < WN; ++a) {
+            if constexpr (kFp4) f.w[a] = *reinterpret_cast<const v4i*>(wq + buf * 256 * 64 + wrow(a) * 64);
+            else f.w[a] = load_frag(wlo, whi, buf * 256 * 128 + wrow(a) * 128);
+        }
     };
 
     v4f acc[WN][TM];
@@ -669,8 +726,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         acc[a][t] += f.sc[si][t] * P[k % kRing];
     };
     // LDS reads of load_tail (first half) and load_head (second half), spread over the MFMAs
-    constexpr int DS_TAIL = (WN + NMF / 2 - 1) / (NMF / 2);
-    constexpr int DS_HEAD = (2 * TM + WN + TM + 2 + (kGemm1 ? 0 : TM) + NMF / 2 - 1) / (NMF / 2);
+    constexpr int WREADS = kFp4 ? WN / 2 : WN;  // LDS reads of half the weight fragments
+    constexpr int DS_TAIL = (WREADS + NMF / 2 - 1) / (NMF / 2);
+    constexpr int DS_HEAD = (2 * TM + WREADS + (kFp4 ? WN : 0) + TM + 2 + (kGemm1 ? 0 : TM) + NMF / 2 - 1) / (NMF / 2);
 
     // One K step s on stage buf, operands in F[par] (read during step s-1).  Half-way through, after
     // the wait for stage s+1 and a barrier (every wave has finished reading stage s by then), stage
@@ -695,7 +753,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                 issue_dma(ic<buf>{});
                 load_head(fn, ic<(buf + 1) % kStages>{});
             }
-            P[i % kRing] = mfma_fp8(fc.w[i / TM], fc.x[i % TM], v4f{0.f, 0.f, 0.f, 0.f});
+            if constexpr (kFp4) P[i % kRing] = mfma_fp4w(fc.w[i / TM], fc.x[i % TM], fc.ws[i / TM], v4f{0.f, 0.f, 0.f, 0.f});
+            else P[i % kRing] = mfma_fp8(fc.w[i / TM], fc.x[i % TM], v4f{0.f, 0.f, 0.f, 0.f});
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
             if (i >= kLag) promote(fc, i - kLag);
             else promote(fn, NMF + i - kLag);                        // previous step's last MFMAs
@@ -769,11 +828,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     if constexpr (kFill) sched_exit(p, nblocks, tid);
 }
 
-template <int BM, bool kGemm1, bool kFill = false, bool kStreamW = false>
+template <int BM, bool kGemm1, bool kFill = false, bool kStreamW = false, bool kFp4 = false>
 hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     int grid = (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kFill, kStreamW>), dim3(grid), dim3(kWaves * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kFill, kStreamW, kFp4>), dim3(grid), dim3(kWaves * 64),
+                       0, stream, p);
     return hipGetLastError();
 }
 
@@ -784,6 +843,9 @@ bool weights_stream(const Params& p) { return (double)p.S * p.T_max * p.K / p.E 
 }  // namespace
 
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
+    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4)
+        return p.BM == 64 ? launch<64, true, false, false, true>(p, num_cus, stream)
+                          : launch<128, true, false, false, true>(p, num_cus, stream);
     if (fuse_fill)
         return p.BM == 64 ? launch<64, true, true>(p, num_cus, stream) : launch<128, true, true>(p, num_cus, stream);
     if (p.BM == 64)
@@ -792,6 +854,9 @@ hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_
 }
 
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream) {
+    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4)
+        return p.BM == 64 ? launch<64, false, false, false, true>(p, num_cus, stream)
+                          : launch<128, false, false, false, true>(p, num_cus, stream);
     if (p.BM == 64)
         return weights_stream(p) ? launch<64, false, false, true>(p, num_cus, stream) : launch<64, false>(p, num_cus, stream);
     return launch<128, false>(p, num_cus, stream);

@@ -62,6 +62,11 @@ int32_t check_config(const mega_moe_config* c) {
     // the shared expert reads the own shard and takes combine slot K (a lane of the combine's ballot)
     if (c->num_shared_experts < 0 || c->num_shared_experts > 1) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->num_shared_experts && (c->local_rank >= c->num_shards || c->topk >= 64)) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (c->weight_format != MEGA_MOE_WEIGHTS_FP8 && c->weight_format != MEGA_MOE_WEIGHTS_MXFP4)
+        return MEGA_MOE_ERR_UNSUPPORTED;
+    // the arrival-counted fill is built for FP8 weights only
+    if (c->weight_format == MEGA_MOE_WEIGHTS_MXFP4 && (c->flags & MEGA_MOE_FLAG_FILL_IN_GEMM1))
+        return MEGA_MOE_ERR_UNSUPPORTED;
     // pool rows and combine rows (K*S*T_max) are int32 / uint32 indices in the kernels
     if ((int64_t)c->num_shards * c->max_tokens_per_shard * (c->topk + 1) + (int64_t)c->num_local_experts * 128 +
             (int64_t)c->max_tokens_per_shard + 128 >=
@@ -169,7 +174,7 @@ int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const 
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MEGA_MOE_ERR_HIP;
     if (mm::launch_pack(w1, w2, w1_packed, w2_packed, cfg->num_local_experts + cfg->num_shared_experts, cfg->hidden,
-                        cfg->intermediate, cus,
+                        cfg->intermediate, cfg->weight_format == MEGA_MOE_WEIGHTS_MXFP4, cus,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
         return MEGA_MOE_ERR_HIP;
     return MEGA_MOE_OK;
@@ -242,6 +247,7 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
     p.El = c.num_local_experts;
     p.nsh = c.num_shared_experts;
     p.own = c.local_rank;
+    p.wfmt = c.weight_format;
     p.lo = c.local_rank * c.num_local_experts;
     p.K = c.topk;
     p.BM = h->lay.block_m;

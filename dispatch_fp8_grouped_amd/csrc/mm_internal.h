@@ -24,6 +24,7 @@ struct Params {
     int S, T_max, H, I, E, El, lo, K, BM;
     int nsh;              // shared experts (0 or 1): pool segment El, weights index El, combine slot K
     int own;              // the shard the shared expert reads (local_rank)
+    int wfmt;             // MEGA_MOE_WEIGHTS_FP8 or MEGA_MOE_WEIGHTS_MXFP4
     int chunks;           // routing chunks per shard
     int max_blocks;       // pool capacity in BM blocks
     uint32_t flags;
@@ -69,8 +70,8 @@ hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream);
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
-hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, int num_cus,
-                       hipStream_t stream);
+hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
+                       int num_cus, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -7,6 +7,8 @@
 //   W1 [E_l][2I][H] -> [E_l][I/128][H/128][256][128]: row r < 128 is gate row nt*128 + r, row r >= 128 is
 //                     up row I + nt*128 + (r - 128)
 //   W2 [E_l][H][I]  -> [E_l][H/256][I/128][256][128]: row r is W2 row nt*256 + r
+// MXFP4 weights (two e2m1 codes per byte) pack the same way with 64-byte rows per 128-value K step:
+//   W1 [E_l][2I][H/2] -> [E_l][I/128][H/128][256][64], W2 [E_l][H][I/2] -> [E_l][H/256][I/128][256][64].
 //
 // One thread per 16-byte piece of the packed tensor (contiguous stores).
 #include "mm_internal.h"
@@ -18,15 +20,17 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kPackThreads = 256;
 
-// gate_up: W1 (rows of an n tile are 128 gate rows then 128 up rows); otherwise W2 (256 consecutive rows)
-template <bool kGateUp>
+// gate_up: W1 (rows of an n tile are 128 gate rows then 128 up rows); otherwise W2 (256 consecutive rows).
+// P: 16-byte pieces per row and K step (8 for FP8, 4 for two FP4 codes per byte).
+template <bool kGateUp, int P>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const v4i* __restrict__ src, v4i* __restrict__ dst,
                                                             int rows, int K, int I, long pieces) {
     const int KB = K >> 7;
+    const long row_pieces = (long)KB * P;           // 16-byte pieces of one source row
     for (long o = (long)blockIdx.x * kPackThreads + threadIdx.x; o < pieces; o += (long)gridDim.x * kPackThreads) {
-        // o = ((((le * NT + nt) * KB + kb) * 256 + r) * 8 + j)
-        const int j = (int)(o & 7);
-        long q = o >> 3;
+        // o = ((((le * NT + nt) * KB + kb) * 256 + r) * P + j)
+        const int j = (int)(o % P);
+        long q = o / P;
         const int r = (int)(q & 255);
         q >>= 8;
         const int kb = (int)(q % KB);
@@ -35,25 +39,35 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const v4i* __restric
         const int nt = (int)(q % NT);
         const long le = q / NT;
         const int row = kGateUp ? (r < 128 ? nt * 128 + r : I + nt * 128 + r - 128) : nt * 256 + r;
-        dst[o] = src[((le * rows + row) * (long)K + kb * 128) / 16 + j];
+        dst[o] = src[(le * rows + row) * row_pieces + (long)kb * P + j];
     }
 }
 
 }  // namespace
 
-hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, int num_cus,
-                       hipStream_t stream) {
-    const long p1 = (long)El * 2 * I * H / 16, p2 = (long)El * H * I / 16;
+hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
+                       int num_cus, hipStream_t stream) {
+    const int div = fp4 ? 32 : 16;                  // bytes per weight value: 1/2 or 1
+    const long p1 = (long)El * 2 * I * H / div, p2 = (long)El * H * I / div;
     auto grid = [&](long pieces) {
         long g = (pieces + kPackThreads - 1) / kPackThreads;
         const long cap = (long)num_cus * 8;
         return (unsigned)(g < cap ? (g < 1 ? 1 : g) : cap);
     };
-    hipLaunchKernelGGL(pack_kernel<true>, dim3(grid(p1)), dim3(kPackThreads), 0, stream,
+    if (fp4) {
+        hipLaunchKernelGGL((pack_kernel<true, 4>), dim3(grid(p1)), dim3(kPackThreads), 0, stream,
+                           static_cast<const v4i*>(w1), static_cast<v4i*>(w1p), 2 * I, H, I, p1);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((pack_kernel<false, 4>), dim3(grid(p2)), dim3(kPackThreads), 0, stream,
+                           static_cast<const v4i*>(w2), static_cast<v4i*>(w2p), H, I, I, p2);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((pack_kernel<true, 8>), dim3(grid(p1)), dim3(kPackThreads), 0, stream,
                        static_cast<const v4i*>(w1), static_cast<v4i*>(w1p), 2 * I, H, I, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(pack_kernel<false>, dim3(grid(p2)), dim3(kPackThreads), 0, stream,
+    hipLaunchKernelGGL((pack_kernel<false, 8>), dim3(grid(p2)), dim3(kPackThreads), 0, stream,
                        static_cast<const v4i*>(w2), static_cast<v4i*>(w2p), H, I, I, p2);
     return hipGetLastError();
 }

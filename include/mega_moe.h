@@ -78,6 +78,13 @@ extern "C" {
                                                   this forward wrote it turns the output into NaN (uses
                                                   hipMemsetAsync: not for graph capture) */
 
+/* Weight formats (mega_moe_config.weight_format). */
+#define MEGA_MOE_WEIGHTS_FP8 0      /* e4m3fn codes, fp32 scales per 128x128 block                      */
+#define MEGA_MOE_WEIGHTS_MXFP4 1    /* e2m1 codes, two per byte (lower K index in the low nibble), one  */
+                                    /* UE8M0 exponent byte per 32 values along K: the FP8 x FP4 variant */
+                                    /* of the layer ("DeepGEMM Mega MoE symmetric memory deep analysis", */
+                                    /* 10.1-10.2)                                                        */
+
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
 #define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */
                                       /* scatter targets, cumulative stats                              */
@@ -108,6 +115,7 @@ typedef struct mega_moe_config {
                                   /* ("DeepGEMM Mega MoE symmetric memory deep analysis", 4.1, 8.1-8.2, */
                                   /* 9.2: the shared expert reads the rank's own input buffer and        */
                                   /* writes the extra combine slot K locally)                           */
+    int32_t weight_format;        /* MEGA_MOE_WEIGHTS_FP8 (default) or MEGA_MOE_WEIGHTS_MXFP4           */
 } mega_moe_config;
 
 /* Byte offsets of the regions inside the workspace (for tests and tools) plus the resolved sizes. */

@@ -79,10 +79,29 @@ def test_shared_expert_whole_layer(case):
     full_compare(sh, inputs=inp, name=sh.name)
 
 
+# --------------------------------------------------------------- MXFP4 weights (the FP8 x FP4 variant)
+@pytest.mark.parametrize("case", ["bm64", "bm128_ragged"])
+def test_mxfp4_weights_whole_layer(case):
+    """e2m1 weights with UE8M0 exponents per 32 K, applied by the MFMA's scale operand: layout
+    bit-exact, whole output within tolerance against the oracle on the decoded weights."""
+    if case == "bm64":
+        sh = MoEShape("mx64", 3, 120, 512, 256, 32, 8, 4, 64, local_rank=1, weight_format="mxfp4", seed=101)
+        tps = [120, 77, 9]
+    else:
+        sh = MoEShape("mx128", 2, 400, 1024, 512, 16, 8, 4, 128, weight_format="mxfp4", seed=102)
+        tps = [400, 263]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    full_compare(sh, inputs=inp, name=sh.name)
+
+
 # --------------------------------------------------------------- full sizes, sampled values
-@pytest.mark.parametrize("name", ["decode", "skewed", "prefill", "decode_shared"])
+_FULL_VARIANTS = {"decode_shared": dict(num_shared_experts=1), "decode_mxfp4": dict(weight_format="mxfp4"),
+                  "prefill_mxfp4": dict(weight_format="mxfp4")}
+
+
+@pytest.mark.parametrize("name", ["decode", "skewed", "prefill", "decode_shared", "decode_mxfp4", "prefill_mxfp4"])
 def test_full_size_layout_and_sampled_tokens(name):
-    shape = SHAPES[name] if name in SHAPES else SHAPES["decode"].replace(name=name, num_shared_experts=1)
+    shape = SHAPES[name] if name in SHAPES else SHAPES[name.split("_")[0]].replace(name=name, **_FULL_VARIANTS[name])
     _print_case(name, shape)
     run = Run(shape)
     inp = inputs_np(run)
