@@ -48,7 +48,8 @@ NUM_STAGES = 5
 STAGE_NAMES = ("route", "fill", "gemm1", "gemm2", "combine")
 
 # Exported symbols of include/mega_moe.h
-EXPORTS = ("mega_moe_workspace_bytes", "mega_moe_init", "mega_moe_pack_weights", "mega_moe_forward",
+EXPORTS = ("mega_moe_workspace_bytes", "mega_moe_init", "mega_moe_pack_weights", "mega_moe_pack_scales",
+           "mega_moe_forward",
            "mega_moe_forward_stages",
            "mega_moe_query_layout", "mega_moe_status", "mega_moe_set_timing", "mega_moe_stage_times",
            "mega_moe_destroy", "mega_moe_strerror")
@@ -99,6 +100,7 @@ def lib():
         L.mega_moe_workspace_bytes.argtypes = [ctypes.POINTER(mega_moe_config), ctypes.POINTER(u64)]
         L.mega_moe_init.argtypes = [ctypes.POINTER(mega_moe_config), vp, u64, vp, ctypes.POINTER(vp)]
         L.mega_moe_pack_weights.argtypes = [ctypes.POINTER(mega_moe_config), vp, vp, vp, vp, vp]
+        L.mega_moe_pack_scales.argtypes = [ctypes.POINTER(mega_moe_config), vp, vp, vp, vp, vp]
         fwd = [vp, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mega_moe_forward.argtypes = fwd
         L.mega_moe_forward_stages.argtypes = [vp, u32] + fwd[1:]
@@ -185,6 +187,12 @@ def mega_moe_pack_weights(cfg: mega_moe_config, w1, w2, w1_packed, w2_packed, st
     _check(rc, "mega_moe_pack_weights")
 
 
+def mega_moe_pack_scales(cfg: mega_moe_config, w1_sf, w2_sf, w1_sf_packed, w2_sf_packed, stream=None):
+    rc = lib().mega_moe_pack_scales(ctypes.byref(cfg), _ptr(w1_sf), _ptr(w2_sf), _ptr(w1_sf_packed),
+                                    _ptr(w2_sf_packed), _stream(stream))
+    _check(rc, "mega_moe_pack_scales")
+
+
 def mega_moe_forward(h, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y,
                      cum_recv_stats=None, stream=None):
     rc = lib().mega_moe_forward(h, _tps_array(tokens_per_shard), _ptr(x), _ptr(x_sf), _ptr(topk_idx),
@@ -267,7 +275,8 @@ class MegaMoE:
                 ("w1 (packed)", w1, self.packed_shapes()[0], torch.uint8),
                 ("w2 (packed)", w2, self.packed_shapes()[1], torch.uint8)]
         if c.weight_format == WEIGHTS_MXFP4:
-            want += [("w1_sf", w1_sf, (El, 2 * I, H // 32), torch.uint8), ("w2_sf", w2_sf, (El, H, I // 32), torch.uint8)]
+            s1, s2 = self.packed_scale_shapes()
+            want += [("w1_sf (packed)", w1_sf, s1, torch.uint8), ("w2_sf (packed)", w2_sf, s2, torch.uint8)]
         else:
             want += [("w1_sf", w1_sf, (El, 2 * I // 128, H // 128), torch.float32),
                      ("w2_sf", w2_sf, (El, H // 128, I // 128), torch.float32)]
@@ -285,6 +294,26 @@ class MegaMoE:
         El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
         rb = 64 if c.weight_format == WEIGHTS_MXFP4 else 128     # bytes per row and 128-value K step
         return (El, I // 128, H // 128, 256, rb), (El, H // 256, I // 128, 256, rb)
+
+    def packed_scale_shapes(self):
+        """Shapes of the packed MXFP4 exponents (see mega_moe_pack_scales)."""
+        c = self.cfg
+        El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
+        return (El, I // 128, H // 128, 256, 4), (El, H // 256, I // 128, 256, 4)
+
+    def pack_scales(self, w1_sf, w2_sf, stream=None):
+        """MXFP4 exponents, uint8 [E_w,2I,H/32] and [E_w,H,I/32] -> new packed tensors (w1_sfp, w2_sfp)."""
+        import torch
+        c = self.cfg
+        El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
+        for name, t, shape in (("w1_sf", w1_sf, (El, 2 * I, H // 32)), ("w2_sf", w2_sf, (El, H, I // 32))):
+            if tuple(t.shape) != shape or t.dtype != torch.uint8 or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"{name}: want contiguous cuda uint8 {shape}, got {t.dtype} {tuple(t.shape)}")
+        s1, s2 = self.packed_scale_shapes()
+        p1 = torch.empty(s1, dtype=torch.uint8, device=w1_sf.device)
+        p2 = torch.empty(s2, dtype=torch.uint8, device=w2_sf.device)
+        mega_moe_pack_scales(self.cfg, w1_sf, w2_sf, p1, p2, stream)
+        return p1, p2
 
     def pack_weights(self, w1, w2, stream=None):
         """Row-major W1 [E_w,2I,H] and W2 [E_w,H,I] (uint8 e4m3fn; E_w = E_l + shared experts, the shared
@@ -317,12 +346,18 @@ class MegaMoE:
     def __call__(self, inputs: dict, y=None, cum_recv_stats=None, stream=None, stages=STAGE_ALL):
         """Forward on an input dict.  The packed weights are taken from inputs["w1_packed"] /
         inputs["w2_packed"]; when absent they are packed from inputs["w1"] / inputs["w2"] once and stored
-        there (the one-time weight transform)."""
+        there (the one-time weight transform).  MXFP4 exponents are packed the same way into
+        inputs["w1_sf_packed"] / inputs["w2_sf_packed"]."""
         if "w1_packed" not in inputs or "w2_packed" not in inputs:
             inputs["w1_packed"], inputs["w2_packed"] = self.pack_weights(inputs["w1"], inputs["w2"], stream)
+        s1, s2 = inputs["w1_sf"], inputs["w2_sf"]
+        if self.cfg.weight_format == WEIGHTS_MXFP4:
+            if "w1_sf_packed" not in inputs or "w2_sf_packed" not in inputs:
+                inputs["w1_sf_packed"], inputs["w2_sf_packed"] = self.pack_scales(s1, s2, stream)
+            s1, s2 = inputs["w1_sf_packed"], inputs["w2_sf_packed"]
         return self.forward(inputs["tokens_per_shard"], inputs["x"], inputs["x_sf"], inputs["topk_idx"],
-                            inputs["topk_weights"], inputs["w1_packed"], inputs["w1_sf"], inputs["w2_packed"],
-                            inputs["w2_sf"], y, cum_recv_stats, stream, stages)
+                            inputs["topk_weights"], inputs["w1_packed"], s1, inputs["w2_packed"],
+                            s2, y, cum_recv_stats, stream, stages)
 
     def status(self, stream=None) -> int:
         return mega_moe_status(self.h, stream)

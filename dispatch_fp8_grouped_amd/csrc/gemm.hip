@@ -468,9 +468,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const uint8_t* iA;
     const uint8_t* iW;
     const uint8_t* iSm;     // per lane
-    const uint8_t* iWs;     // per lane (MXFP4): the exponent bytes of this lane's weight row
+    const uint8_t* iWs;     // per lane (MXFP4): the exponent word of this lane's weight row
     // MXFP4: the tile row whose exponents this lane loads, fragment lane >> 4, row lane & 15 (the rows
-    // the wave's weight fragments cover, in the order they are read back)
+    // the wave's weight fragments cover, in the order they are read back; 32 consecutive rows per half
+    // wave, so one step's exponent load is two 128-byte runs)
     const int ws_tr = kGemm1 ? wn * 32 + ((lane >> 4) < 2 ? 0 : 128) + ((lane >> 4) & 1) * 16 + (lane & 15)
                              : wn * WROWS + (lane >> 4) * 16 + (lane & 15);
     auto set_issue_tile = [&]() __attribute__((always_inline)) {
@@ -486,10 +487,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b) + (size_t)ikc * BM * 128));
         iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt) + (size_t)ikc * 256 * WRB));
         if constexpr (kFp4) {
-            const int grow = kGemm1 ? (ws_tr < 128 ? nt * 128 + ws_tr : p.I + nt * 128 + ws_tr - 128) : nt * 256 + ws_tr;
-            const size_t nrows = kGemm1 ? (size_t)2 * p.I : (size_t)p.H;
+            // packed exponents: [E_w][n tile][K block][256 rows] words, one word = the row's four 32-value blocks
+            const size_t nts = kGemm1 ? (size_t)(p.I >> 7) : (size_t)(p.H >> 8);
             iWs = reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf : p.w2_sf) +
-                  ((size_t)le * nrows + grow) * (size_t)(Kdim >> 5) + (size_t)ikc * 4;
+                  (((size_t)le * nts + nt) * KB + ikc) * 1024 + ws_tr * 4;
         }
         const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (size_t)b * KB * BM + sm_row;
         int blk;
@@ -524,13 +525,13 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                 iA += BM * 128;
                 iW += 256 * WRB;
                 iSm += sm_inc;
-                if constexpr (kFp4) iWs += 4;
+                if constexpr (kFp4) iWs += 1024;
             } else {                                    // wrap to K block 0
                 ikc = 0;
                 iA -= (size_t)(KB - 1) * BM * 128;
                 iW -= (size_t)(KB - 1) * 256 * WRB;
                 iSm -= (size_t)(KB - 1) * sm_inc;
-                if constexpr (kFp4) iWs -= (size_t)(KB - 1) * 4;
+                if constexpr (kFp4) iWs -= (size_t)(KB - 1) * 1024;
             }
         } else if (ij + 1 < my_tiles) {
             ikb = 0;

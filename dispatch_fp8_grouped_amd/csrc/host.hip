@@ -180,6 +180,26 @@ int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const 
     return MEGA_MOE_OK;
 }
 
+int32_t mega_moe_pack_scales(const mega_moe_config* cfg, const void* w1_sf, const void* w2_sf, void* w1_sf_packed,
+                             void* w2_sf_packed, void* stream) {
+    if (!cfg || !w1_sf || !w2_sf || !w1_sf_packed || !w2_sf_packed) return MEGA_MOE_ERR_INVALID_ARG;
+    const int32_t rc = check_config(cfg);
+    if (rc) return rc;
+    if (cfg->weight_format != MEGA_MOE_WEIGHTS_MXFP4) return MEGA_MOE_ERR_INVALID_ARG;
+    auto aligned4 = [](const void* q) { return ((uintptr_t)q & 3) == 0; };
+    if (!aligned4(w1_sf) || !aligned4(w2_sf) || !aligned4(w1_sf_packed) || !aligned4(w2_sf_packed))
+        return MEGA_MOE_ERR_INVALID_ARG;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return MEGA_MOE_ERR_HIP;
+    if (mm::launch_pack_scales(w1_sf, w2_sf, w1_sf_packed, w2_sf_packed,
+                               cfg->num_local_experts + cfg->num_shared_experts, cfg->hidden, cfg->intermediate, cus,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MEGA_MOE_ERR_HIP;
+    return MEGA_MOE_OK;
+}
+
 int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t workspace_bytes, void* stream,
                       mega_moe_handle** out) {
     if (!cfg || !out) return MEGA_MOE_ERR_INVALID_ARG;

@@ -72,6 +72,9 @@ hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
 hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
                        int num_cus, hipStream_t stream);
+// MXFP4 exponent transform: [E_w][2I][H/32] / [E_w][H][I/32] bytes -> [E_w][NT][K/128][256] words.
+hipError_t launch_pack_scales(const void* s1, const void* s2, void* s1p, void* s2p, int El, int H, int I,
+                              int num_cus, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

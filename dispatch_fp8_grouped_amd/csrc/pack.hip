@@ -9,8 +9,11 @@
 //   W2 [E_l][H][I]  -> [E_l][H/256][I/128][256][128]: row r is W2 row nt*256 + r
 // MXFP4 weights (two e2m1 codes per byte) pack the same way with 64-byte rows per 128-value K step:
 //   W1 [E_l][2I][H/2] -> [E_l][I/128][H/128][256][64], W2 [E_l][H][I/2] -> [E_l][H/256][I/128][256][64].
+// Their UE8M0 exponents (one byte per 32 values along K) follow the same chunking, four bytes per row and
+// K step, so that one GEMM step reads a chunk's exponents as 1 KB of consecutive words:
+//   W1 exponents [E_l][2I][H/32] -> [E_l][I/128][H/128][256] words, W2 [E_l][H][I/32] -> [E_l][H/256][I/128][256].
 //
-// One thread per 16-byte piece of the packed tensor (contiguous stores).
+// One thread per 16-byte piece of the packed tensor (contiguous stores); one per word for the exponents.
 #include "mm_internal.h"
 
 namespace mm {
@@ -43,17 +46,50 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const v4i* __restric
     }
 }
 
+// MXFP4 exponents: word (le, nt, kb, r) = the four bytes of packed row r for K step kb.
+template <bool kGateUp>
+__global__ __launch_bounds__(kPackThreads) void pack_scales_kernel(const uint32_t* __restrict__ src,
+                                                                   uint32_t* __restrict__ dst, int rows, int K,
+                                                                   int I, long words) {
+    const int KB = K >> 7;                          // source row: K/32 bytes = KB words
+    const int NT = kGateUp ? (I >> 7) : (rows >> 8);
+    for (long o = (long)blockIdx.x * kPackThreads + threadIdx.x; o < words; o += (long)gridDim.x * kPackThreads) {
+        const int r = (int)(o & 255);
+        long q = o >> 8;
+        const int kb = (int)(q % KB);
+        q /= KB;
+        const int nt = (int)(q % NT);
+        const long le = q / NT;
+        const int row = kGateUp ? (r < 128 ? nt * 128 + r : I + nt * 128 + r - 128) : nt * 256 + r;
+        dst[o] = src[(le * rows + row) * KB + kb];
+    }
+}
+
+long pack_grid(long items, int num_cus) {
+    long g = (items + kPackThreads - 1) / kPackThreads;
+    const long cap = (long)num_cus * 8;
+    return g < cap ? (g < 1 ? 1 : g) : cap;
+}
+
 }  // namespace
+
+hipError_t launch_pack_scales(const void* s1, const void* s2, void* s1p, void* s2p, int El, int H, int I,
+                              int num_cus, hipStream_t stream) {
+    const long n1 = (long)El * 2 * I * H / 128, n2 = (long)El * H * I / 128;   // words
+    hipLaunchKernelGGL((pack_scales_kernel<true>), dim3((unsigned)pack_grid(n1, num_cus)), dim3(kPackThreads), 0,
+                       stream, static_cast<const uint32_t*>(s1), static_cast<uint32_t*>(s1p), 2 * I, H, I, n1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((pack_scales_kernel<false>), dim3((unsigned)pack_grid(n2, num_cus)), dim3(kPackThreads), 0,
+                       stream, static_cast<const uint32_t*>(s2), static_cast<uint32_t*>(s2p), H, I, I, n2);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
                        int num_cus, hipStream_t stream) {
     const int div = fp4 ? 32 : 16;                  // bytes per weight value: 1/2 or 1
     const long p1 = (long)El * 2 * I * H / div, p2 = (long)El * H * I / div;
-    auto grid = [&](long pieces) {
-        long g = (pieces + kPackThreads - 1) / kPackThreads;
-        const long cap = (long)num_cus * 8;
-        return (unsigned)(g < cap ? (g < 1 ? 1 : g) : cap);
-    };
+    auto grid = [&](long pieces) { return (unsigned)pack_grid(pieces, num_cus); };
     if (fp4) {
         hipLaunchKernelGGL((pack_kernel<true, 4>), dim3(grid(p1)), dim3(kPackThreads), 0, stream,
                            static_cast<const v4i*>(w1), static_cast<v4i*>(w1p), 2 * I, H, I, p1);

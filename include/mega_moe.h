@@ -182,10 +182,29 @@ int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t work
  *   w2_packed  uint8 [E_w][H/256][I/128][256][128]: chunk (le, nt, kb), row r, byte j holds
  *              W2[le][nt*256 + r][kb*128 + j]
  * w1 / w2 are the row-major [E_w][2I][H] / [E_w][H][I] e4m3fn tensors below; the packed buffers have the
- * same byte counts and must not overlap them.  Asynchronous on `stream`; no handle is needed.
+ * same byte counts and must not overlap them.
+ * With weight_format MEGA_MOE_WEIGHTS_MXFP4 the inputs are the e2m1 codes, uint8 [E_w][2I][H/2] and
+ * [E_w][H][I/2], and each packed row holds 64 bytes per K step: w1_packed [E_w][I/128][H/128][256][64],
+ * w2_packed [E_w][H/256][I/128][256][64], same row order.
+ * Asynchronous on `stream`; no handle is needed.
  * Errors: INVALID_ARG (null or not 16-byte aligned pointer), UNSUPPORTED (config), HIP. */
 int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const void* w2, void* w1_packed,
                               void* w2_packed, void* stream);
+
+/* One-time transform of MXFP4 weight exponents (weight_format MEGA_MOE_WEIGHTS_MXFP4 only).  The pages
+ * pass the FP4 kernel's scale factors packed along K and transposed for the kernel ("DeepGEMM Mega MoE
+ * symmetric memory deep analysis", 10.1-10.2); here they follow the packed weights' chunks, so one GEMM
+ * step reads a chunk's exponents as 1 KB of consecutive words:
+ *   w1_sf          uint8 [E_w][2I][H/32]: UE8M0 exponent of W1[le][n][32j .. 32j+31] at [le][n][j]
+ *   w2_sf          uint8 [E_w][H][I/32]
+ *   w1_sf_packed   uint8 [E_w][I/128][H/128][256][4]: chunk (le, nt, kb), row r, byte j holds
+ *                  w1_sf[le][r < 128 ? nt*128 + r : I + nt*128 + r - 128][4*kb + j]
+ *   w2_sf_packed   uint8 [E_w][H/256][I/128][256][4]: byte j of (le, nt, kb, r) holds w2_sf[le][nt*256 + r][4*kb + j]
+ * The packed buffers have the same byte counts as the inputs and must not overlap them.  Asynchronous on
+ * `stream`; no handle is needed.
+ * Errors: INVALID_ARG (null or not 4-byte aligned pointer, or an FP8 config), UNSUPPORTED (config), HIP. */
+int32_t mega_moe_pack_scales(const mega_moe_config* cfg, const void* w1_sf, const void* w2_sf, void* w1_sf_packed,
+                             void* w2_sf_packed, void* stream);
 
 /* The whole layer.  Shapes (S, T_max, H, I, E_l, K from the config):
  *   tokens_per_shard  host int32 [S], each in 0..T_max: valid tokens of each shard (rows t >= T_s are
@@ -199,6 +218,9 @@ int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const 
  *   w1_sf             float [E_w][2I/128][H/128], 128x128 block scales of the unpacked W1
  *   w2                W2 packed by mega_moe_pack_weights from uint8 [E_w][H][I] e4m3fn
  *   w2_sf             float [E_w][H/128][I/128]
+ *                     With weight_format MEGA_MOE_WEIGHTS_MXFP4: w1 / w2 are the packed e2m1 codes and
+ *                     w1_sf / w2_sf the exponents packed by mega_moe_pack_scales (uint8, passed through
+ *                     the same float pointers)
  *   y                 bf16 [S][T_max][H] output: y[s,t] = sum over k with a local expert of
  *                     w[s,t,k] * Expert(x[s,t]), plus Shared(x[s,t]) for s = local_rank when the
  *                     config has a shared expert; a token with nothing to add gets a zero row

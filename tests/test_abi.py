@@ -165,3 +165,15 @@ def test_weight_format_config():
     for c in (cfg_of("decode", weight_format=2), cfg_of("decode", weight_format=-1),
               cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_FILL_IN_GEMM1)):
         assert lib.mega_moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == mm.ERR_UNSUPPORTED
+
+
+def test_pack_scales_argument_checks():
+    """The exponent transform exists for MXFP4 only: an FP8 config, null and misaligned pointers are
+    rejected before any device work (no GPU needed)."""
+    import ctypes
+    lib = mm.lib()
+    a = ctypes.c_void_p(4096)
+    fp8, mx = cfg_of("decode"), cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4)
+    assert lib.mega_moe_pack_scales(ctypes.byref(fp8), a, a, a, a, None) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_pack_scales(ctypes.byref(mx), None, a, a, a, None) == mm.ERR_INVALID_ARG
+    assert lib.mega_moe_pack_scales(ctypes.byref(mx), a, ctypes.c_void_p(4098), a, a, None) == mm.ERR_INVALID_ARG

@@ -194,6 +194,29 @@ def test_pack_weights_layout():
     moe.close()
 
 
+def test_pack_scales_layout():
+    """The packed MXFP4 exponents hold every byte of the row-major exponents at the documented position:
+    chunk (le, nt, kb), row r, byte j = exponent block 4*kb + j of the chunk's weight row r."""
+    print("[case] mxfp4 exponent pack layout", flush=True)
+    sh = MoEShape("packsf", 1, 8, 512, 384, 6, 3, 2, 64, seed=27, weight_format="mxfp4")
+    inp = on_gpu(make_inputs(sh))
+    moe = mm.MegaMoE.from_shape(sh)
+    s1p, s2p = moe.pack_scales(inp["w1_sf"], inp["w2_sf"])
+    torch.cuda.synchronize()
+    El, H, I = sh.num_local_experts, sh.hidden, sh.intermediate
+    s1 = inp["w1_sf"].cpu().numpy()
+    s2 = inp["w2_sf"].cpu().numpy()
+    want1 = np.empty((El, I // 128, H // 128, 256, 4), np.uint8)
+    for nt in range(I // 128):
+        for r in range(256):
+            row = nt * 128 + r if r < 128 else I + nt * 128 + r - 128
+            want1[:, nt, :, r, :] = s1[:, row, :].reshape(El, H // 128, 4)
+    want2 = s2.reshape(El, H // 256, 256, I // 128, 4).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(s1p.cpu().numpy(), want1)
+    assert np.array_equal(s2p.cpu().numpy(), want2)
+    moe.close()
+
+
 def test_stage_timing():
     sh = SHAPES["tiny"]
     inp = on_gpu(make_inputs(sh))
