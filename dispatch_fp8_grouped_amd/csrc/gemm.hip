@@ -844,9 +844,12 @@ bool weights_stream(const Params& p) { return (double)p.S * p.T_max * p.K / p.E 
 }  // namespace
 
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
-    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4)
-        return p.BM == 64 ? launch<64, true, false, false, true>(p, num_cus, stream)
-                          : launch<128, true, false, false, true>(p, num_cus, stream);
+    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
+        if (p.BM == 64)
+            return weights_stream(p) ? launch<64, true, false, true, true>(p, num_cus, stream)
+                                     : launch<64, true, false, false, true>(p, num_cus, stream);
+        return launch<128, true, false, false, true>(p, num_cus, stream);
+    }
     if (fuse_fill)
         return p.BM == 64 ? launch<64, true, true>(p, num_cus, stream) : launch<128, true, true>(p, num_cus, stream);
     if (p.BM == 64)
@@ -855,9 +858,12 @@ hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_
 }
 
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream) {
-    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4)
-        return p.BM == 64 ? launch<64, false, false, false, true>(p, num_cus, stream)
-                          : launch<128, false, false, false, true>(p, num_cus, stream);
+    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
+        if (p.BM == 64)
+            return weights_stream(p) ? launch<64, false, false, true, true>(p, num_cus, stream)
+                                     : launch<64, false, false, false, true>(p, num_cus, stream);
+        return launch<128, false, false, false, true>(p, num_cus, stream);
+    }
     if (p.BM == 64)
         return weights_stream(p) ? launch<64, false, false, true>(p, num_cus, stream) : launch<64, false>(p, num_cus, stream);
     return launch<128, false>(p, num_cus, stream);
