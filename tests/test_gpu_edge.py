@@ -316,20 +316,23 @@ def test_fill_inside_gemm1_matches_separate_fill(case):
         r.close()
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("wf", ["fp8", "mxfp4"])
+def test_graph_capture_replays_match_eager(wf):
     """One forward captured in a HIP graph: three replays on changing input contents, with eager
     forwards and synchronisations between them, each bit-identical to the eager forward on the same
     inputs (the forward records no memset and leaves its workspace counters at zero)."""
-    print("[case] graph capture and replays", flush=True)
-    sh = MoEShape("graph", 4, 96, 512, 256, 32, 8, 4, 64, local_rank=1, seed=61)
+    print(f"[case] graph capture and replays, {wf} weights", flush=True)
+    sh = MoEShape("graph", 4, 96, 512, 256, 32, 8, 4, 64, local_rank=1, weight_format=wf, seed=61)
     tps = [96, 50, 0, 77]
     a = on_gpu(make_inputs(sh, tokens_per_shard=tps))
     b = on_gpu(make_inputs(sh, seed=62, tokens_per_shard=tps))
     for k in ("w1", "w1_sf", "w2", "w2_sf"):
         b[k] = a[k]
     moe = mm.MegaMoE.from_shape(sh)
-    moe(a)                                   # packs a's weights into a["w1_packed"], a["w2_packed"]
-    b["w1_packed"], b["w2_packed"] = a["w1_packed"], a["w2_packed"]
+    moe(a)                                   # packs a's weights (and MXFP4 exponents) into a
+    for k in ("w1_packed", "w2_packed", "w1_sf_packed", "w2_sf_packed"):
+        if k in a:
+            b[k] = a[k]
     ya, yb = moe(a), moe(b)
     torch.cuda.synchronize()
     dyn = ("x", "x_sf", "topk_idx", "topk_weights")
