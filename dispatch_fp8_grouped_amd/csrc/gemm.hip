@@ -20,11 +20,12 @@
 //   GEMM2: hidden rows nt*256 + wn*64 + [0,64).
 //
 // Pipeline: a K step's operands (A and B tiles, the token scales, the two weight-block scales and, for
-// GEMM2, the tile's pool metadata) arrive by LDS DMA (global_load_lds) into one of three LDS stages.
+// GEMM2, the tile's pool metadata) arrive by LDS DMA (global_load_lds) into one of N LDS stages (three;
+// four for MXFP4 weights at BLOCK_M 128, whose stages are smaller).
 // The persistent work-group walks its (tile, K step) sequence as one stream.  Step s computes from
 // registers that were read from LDS during step s-1; half-way through, it waits until stage s+1 has
-// landed (vmcnt lets only the youngest DMA group stay in flight), barriers, refills its own stage with
-// step s+3 and reads stage s+1 into the second register set while its remaining MFMAs run.  The next
+// landed (vmcnt lets the N-2 youngest DMA groups stay in flight), barriers, refills its own stage with
+// step s+N and reads stage s+1 into the second register set while its remaining MFMAs run.  The next
 // tile's first steps load during the current tile's last ones.  Every step issues the same number of
 // DMA instructions (past the end the last step is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
 // XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
@@ -44,7 +45,11 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
-constexpr int kStages = 3;
+// LDS stages of the load pipeline (steps in flight = stages - 1).  FP8 stages (48 or 40 KB) fit three
+// times in the 160 KB of LDS.  MXFP4's halved weight chunk leaves room for more: a fourth stage (146 KB)
+// took the prefill-shaped MXFP4 layer from 1.80 to 1.78 ms; at BLOCK_M 64 (decode), five stages (141 KB)
+// were no faster than three, so that launch keeps three.
+constexpr int stages_of(int BM, bool fp4) { return fp4 && BM == 128 ? 4 : 3; }
 
 // MXFP4 weight fragment (16 rows x 128 K as e2m1, 16 bytes per lane) times an FP8 token fragment; the
 // weight rows' UE8M0 exponents come in through the MFMA's A-scale operand (byte 0 of `sa`, one per lane:
@@ -364,6 +369,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     static_assert(A_INS >= 1 && B_INS >= 1 && 2 * SA_LANES + 2 <= 64, "tile shape");
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
     static_assert(kGemm1 || !kFill, "the fill feeds GEMM1 only");
+    constexpr int kStages = stages_of(BM, kFp4);
+    constexpr int kInFlight = (kStages - 2) * DMA_PER_STEP;   // at mid-step: the steps after the next one
+    static_assert((kStages - 1) * DMA_PER_STEP + kEpiStores < 64, "vmcnt immediate");
 
     __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * WRB];
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 
     // One K step s on stage buf, operands in F[par] (read during step s-1).  Half-way through, after
     // the wait for stage s+1 and a barrier (every wave has finished reading stage s by then), stage
-    // buf is refilled with step s+3 and the operands of step s+1 are read into F[par ^ 1] while the
+    // buf is refilled with step s+kStages and the operands of step s+1 are read into F[par ^ 1] while the
     // second half's MFMAs run.  After a tile's last step: the pending promotions, then the epilogue.
     auto step = [&](auto bufc, auto parc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
@@ -748,8 +756,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                 // stage s+1; when step s-1 ended a tile, its epilogue stores are younger than that
                 // stage's DMA and may stay in flight (GEMM2; GEMM1's few stores are cheaper to drain
                 // than the selection)
-                if constexpr (kGemm1) wait_stage_barrier<DMA_PER_STEP>();
-                else wait_stage_barrier_sel<DMA_PER_STEP, DMA_PER_STEP + kEpiStores>(epi_prev);
+                if constexpr (kGemm1) wait_stage_barrier<kInFlight>();
+                else wait_stage_barrier_sel<kInFlight, kInFlight + kEpiStores>(epi_prev);
                 __builtin_amdgcn_sched_barrier(0);
                 issue_dma(ic<buf>{});
                 load_head(fn, ic<(buf + 1) % kStages>{});
@@ -806,25 +814,28 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // step's operands are in flight, and the tile loop itself needs no check
     if constexpr (kFill) spin_until(p, p.sched + kSchedDone, fill_total, lane);
     issue_advance();
-    issue_dma(ic<1>{});
-    issue_advance();
-    issue_dma(ic<2>{});
-    issue_advance();
-    wait_stage_barrier<2 * DMA_PER_STEP>();
+    // the other stages of the prologue
+    auto prologue = [&](auto self, auto ic_j) __attribute__((always_inline)) {
+        constexpr int j = decltype(ic_j)::value;
+        issue_dma(ic<j>{});
+        issue_advance();
+        if constexpr (j + 1 < kStages) self(self, ic<j + 1>{});
+    };
+    prologue(prologue, ic<1>{});
+    wait_stage_barrier<(kStages - 1) * DMA_PER_STEP>();
     load_head(F[0], ic<0>{});
-    for (int s = 0; s < nsteps; s += 2 * kStages) {
-        step(ic<0>{}, ic<0>{});
-        if (s + 1 >= nsteps) break;
-        step(ic<1>{}, ic<1>{});
-        if (s + 2 >= nsteps) break;
-        step(ic<2>{}, ic<0>{});
-        if (s + 3 >= nsteps) break;
-        step(ic<0>{}, ic<1>{});
-        if (s + 4 >= nsteps) break;
-        step(ic<1>{}, ic<0>{});
-        if (s + 5 >= nsteps) break;
-        step(ic<2>{}, ic<1>{});
-    }
+    // Steps s .. s+kUnroll-1 with their stage (I mod kStages) and operand set (I mod 2) fixed at compile
+    // time; false once the last step has run.
+    constexpr int kUnroll = kStages % 2 ? 2 * kStages : kStages;
+    auto steps = [&](int s, auto self, auto ic_i) __attribute__((always_inline)) -> bool {
+        constexpr int I = decltype(ic_i)::value;
+        step(ic<I % kStages>{}, ic<I % 2>{});
+        if (s + I + 1 >= nsteps) return false;
+        if constexpr (I + 1 < kUnroll) return self(s, self, ic<I + 1>{});
+        else return true;
+    };
+    for (int s = 0; s < nsteps; s += kUnroll)
+        if (!steps(s, steps, ic<0>{})) break;
     wait_all_vm();      // no LDS DMA may still be landing when the work-group ends
     if constexpr (kFill) sched_exit(p, nblocks, tid);
 }
