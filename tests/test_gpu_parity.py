@@ -80,12 +80,14 @@ def test_shared_expert_whole_layer(case):
 
 
 # --------------------------------------------------------------- MXFP4 weights (the FP8 x FP4 variant)
-@pytest.mark.parametrize("case", ["bm64", "bm128_ragged", "bm64_shared_empty_shard", "bm128_zipf"])
+@pytest.mark.parametrize("case", ["bm64", "bm128_ragged", "bm64_shared_empty_shard", "bm128_zipf",
+                                  "bm128_short_k", "bm64_short_k"])
 def test_mxfp4_weights_whole_layer(case):
     """e2m1 weights with UE8M0 exponents per 32 K, applied by the MFMA's scale operand: layout
     bit-exact, whole output within tolerance against the oracle on the decoded weights.  Also with a
     shared expert (its MXFP4 weights packed after the routed experts') beside an empty shard, and with
-    skewed routing (some experts with many blocks, some with none)."""
+    skewed routing (some experts with many blocks, some with none), and with K loops shorter than the
+    load pipeline."""
     if case == "bm64":
         sh = MoEShape("mx64", 3, 120, 512, 256, 32, 8, 4, 64, local_rank=1, weight_format="mxfp4", seed=101)
         tps = [120, 77, 9]
@@ -96,10 +98,15 @@ def test_mxfp4_weights_whole_layer(case):
         sh = MoEShape("mx64sh", 3, 130, 512, 384, 24, 8, 4, 64, local_rank=2, num_shared_experts=1,
                       weight_format="mxfp4", seed=103)
         tps = [130, 0, 71]
-    else:
+    elif case == "bm128_zipf":
         sh = MoEShape("mx128z", 4, 256, 768, 256, 32, 8, 4, 128, local_rank=0, routing="zipf",
                       weight_format="mxfp4", seed=104)
         tps = [256, 256, 190, 33]
+    else:
+        # K loops shorter than the load pipeline: GEMM1 has H/128 = 2 steps per tile and GEMM2 I/128 = 1
+        bm = 128 if case == "bm128_short_k" else 64
+        sh = MoEShape("mxshort", 2, 200, 256, 128, 8, 4, 2, bm, local_rank=1, weight_format="mxfp4", seed=105)
+        tps = [200, 141]
     inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
     full_compare(sh, inputs=inp, name=sh.name)
 
