@@ -7,7 +7,11 @@ If the library is not built, loading it raises: there is no fallback path.
     from dispatch_fp8_grouped_amd import MegaMoE
     moe = MegaMoE(num_shards=8, max_tokens_per_shard=4096, hidden=7168, intermediate=2048,
                   num_experts=256, num_local_experts=32, topk=8, block_m=128)
-    y = moe.forward(tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf)
+    w1p, w2p = moe.pack_weights(w1, w2)                 # once: the tiled order the GEMMs stream
+    y = moe.forward(tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1p, w1_sf, w2p, w2_sf)
+
+With MXFP4 weights (weight_format=WEIGHTS_MXFP4) the exponents are packed once as well,
+s1p, s2p = moe.pack_scales(w1_sf, w2_sf), and passed in place of w1_sf / w2_sf.
 """
 from __future__ import annotations
 
