@@ -111,6 +111,44 @@ def test_mxfp4_weights_whole_layer(case):
     full_compare(sh, inputs=inp, name=sh.name)
 
 
+# --------------------------------------------------------------- seeded sweep of small configurations
+def _sweep_cases(n=40, seed=2024):
+    """Random small layers, alternating FP8 and MXFP4 weights: BLOCK_M 64/128, H 256-768, I 128-384,
+    1-16 local experts on 1, 2 or 4 ranks, top-1..8, 1-4 shards with random (possibly zero) token
+    counts, uniform or Zipf routing, with or without a shared expert."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wf = "mxfp4" if i % 2 else "fp8"
+        bm = int(rng.choice([64, 128]))
+        H = int(rng.choice([256, 512, 768]))
+        I = int(rng.choice([128, 256, 384]))
+        El = int(rng.integers(1, 17))
+        R = int(rng.choice([1, 2, 4]))
+        E = El * R
+        K = int(rng.integers(1, min(E, 8) + 1))
+        S = int(rng.integers(1, 5))
+        T = int(rng.integers(1, 257))
+        rank = int(rng.integers(0, R))
+        nsh = int(rng.integers(0, 2)) if rank < S else 0
+        routing = "zipf" if rng.random() < 0.3 else "uniform"
+        tps = [int(rng.integers(0, T + 1)) for _ in range(S)]
+        out.append((MoEShape(f"sweep{i}", S, T, H, I, E, El, K, bm, local_rank=rank, routing=routing,
+                             num_shared_experts=nsh, weight_format=wf, seed=300 + i), tps))
+    return out
+
+
+_SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", range(len(_SWEEP)), ids=[sh.name for sh, _ in _SWEEP])
+def test_random_configs_whole_layer(case):
+    """Layout bit-exact and the whole output within tolerance on each seeded configuration."""
+    sh, tps = _SWEEP[case]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    full_compare(sh, inputs=inp, name=f"{sh.name} {sh.weight_format} tps={tps}")
+
+
 # --------------------------------------------------------------- full sizes, sampled values
 _FULL_VARIANTS = {"decode_shared": dict(num_shared_experts=1), "decode_mxfp4": dict(weight_format="mxfp4"),
                   "prefill_mxfp4": dict(weight_format="mxfp4")}
