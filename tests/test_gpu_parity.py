@@ -149,6 +149,18 @@ def test_random_configs_whole_layer(case):
     full_compare(sh, inputs=inp, name=f"{sh.name} {sh.weight_format} tps={tps}")
 
 
+_SWEEP_FP8 = [i for i, (sh, _) in enumerate(_SWEEP) if sh.weight_format == "fp8"]
+
+
+@pytest.mark.parametrize("case", _SWEEP_FP8, ids=[_SWEEP[i][0].name for i in _SWEEP_FP8])
+def test_random_configs_fill_inside_gemm1(case):
+    """The same FP8 configurations under the arrival-counted schedule (GEMM1's work-groups pull the
+    pool themselves), including those with no routed rows at all."""
+    sh, tps = _SWEEP[case]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    full_compare(sh, inputs=inp, flags=mm.FLAG_FILL_IN_GEMM1, name=f"{sh.name} fill-in-gemm1 tps={tps}")
+
+
 # --------------------------------------------------------------- full sizes, sampled values
 _FULL_VARIANTS = {"decode_shared": dict(num_shared_experts=1), "decode_mxfp4": dict(weight_format="mxfp4"),
                   "prefill_mxfp4": dict(weight_format="mxfp4")}
