@@ -91,6 +91,17 @@ int main() {
     CHECK(mega_moe_init(&c, ws, bytes - 1, nullptr, &h) == MEGA_MOE_ERR_WORKSPACE_TOO_SMALL);
     CHECK(mega_moe_pack_weights(&c, nullptr, ws, ws, ws, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
     CHECK(mega_moe_pack_weights(&c, (char*)ws + 4, ws, ws, ws, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
+    // exponent transform: MXFP4 configs only; null and misaligned pointers rejected before any device work
+    CHECK(mega_moe_pack_scales(&c, ws, ws, ws, ws, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
+    {
+        mega_moe_config mx = c;
+        mx.weight_format = MEGA_MOE_WEIGHTS_MXFP4;
+        CHECK(mega_moe_pack_scales(&mx, nullptr, ws, ws, ws, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
+        CHECK(mega_moe_pack_scales(&mx, ws, (char*)ws + 2, ws, ws, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
+        CHECK(mega_moe_pack_scales(nullptr, ws, ws, ws, ws, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
+        mx.weight_format = 7;
+        CHECK(mega_moe_pack_scales(&mx, ws, ws, ws, ws, nullptr) == MEGA_MOE_ERR_UNSUPPORTED);
+    }
     const int32_t tps[8] = {1, 2, 3, 4, 5, 6, 7, 8};
     CHECK(mega_moe_forward(nullptr, tps, ws, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                            nullptr, nullptr, nullptr) == MEGA_MOE_ERR_INVALID_ARG);
