@@ -111,6 +111,19 @@ def test_mxfp4_weights_whole_layer(case):
     full_compare(sh, inputs=inp, name=sh.name)
 
 
+def test_mxfp4_wide_exponent_range():
+    """Exponent bytes drawn uniformly from [112, 142] (scales 2^-15 .. 2^15), independently per row and
+    32-value block: a scale applied to the wrong lane, K block or byte of the packed word would be off
+    by orders of magnitude, not by a rounding step."""
+    sh = MoEShape("mxwide", 2, 150, 512, 256, 16, 8, 4, 64, local_rank=1, weight_format="mxfp4", seed=106)
+    tps = [150, 99]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    g = torch.Generator().manual_seed(107)
+    for k in ("w1_sf", "w2_sf"):
+        inp[k] = torch.randint(112, 143, tuple(inp[k].shape), generator=g, dtype=torch.int32).to(torch.uint8).cuda()
+    full_compare(sh, inputs=inp, name="mxfp4 wide exponents")
+
+
 # --------------------------------------------------------------- seeded sweep of small configurations
 def _sweep_cases(n=40, seed=2024):
     """Random small layers, alternating FP8 and MXFP4 weights: BLOCK_M 64/128, H 256-768, I 128-384,
