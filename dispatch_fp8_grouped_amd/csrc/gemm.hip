@@ -396,11 +396,14 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t fill_total = (uint32_t)nblocks * FillUnits<BM>::per_block;
     if constexpr (kFill) fill_pool<BM>(p, nblocks, lane);
-    if (logical >= ntiles) {
+    // Full rounds of G tiles go by `logical`; the tiles of a partial last round by the raw work-group
+    // index, which spreads them over all eight XCDs (by `logical` they would all fall on the first few).
+    const int full = ntiles / G;
+    const int my_tiles = full + ((int)blockIdx.x < ntiles - full * G ? 1 : 0);
+    if (my_tiles == 0) {
         if constexpr (kFill) sched_exit(p, nblocks, tid);
         return;
     }
-    const int my_tiles = (ntiles - 1 - logical) / G + 1;
     const int nsteps = my_tiles * KB;
 
     // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // every block of one expert: the blocks' A chunks and the n tiles' W chunks are shared through
     // that XCD's L2, each W tile is fetched by one or two XCDs and each A block about NT/4 times.
     auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
-        const int t = logical + j * G;
+        const int t = j < full ? logical + j * G : full * G + (int)blockIdx.x;
         const int vb = t / NT;
         int lo = 0, hi = nseg;              // the expert with off[le] <= vb < off[le+1]
         while (hi - lo > 1) {
