@@ -227,7 +227,9 @@ def swiglu(g: np.ndarray, intermediate: int) -> np.ndarray:
     """
     gate = g[:, :intermediate]
     up = g[:, intermediate:]
-    return gate / (1.0 + np.exp(-gate)) * up
+    # e^-z overflows to inf for very negative z, and z/inf = -0 is silu's limit there
+    with np.errstate(over="ignore"):
+        return gate / (1.0 + np.exp(-gate)) * up
 
 
 def requant_rows(h: np.ndarray, gran: int = 128):
