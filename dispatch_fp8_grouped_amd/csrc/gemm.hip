@@ -20,8 +20,7 @@
 //   GEMM2: hidden rows nt*256 + wn*64 + [0,64).
 //
 // Pipeline: a K step's operands (A and B tiles, the token scales, the two weight-block scales and, for
-// GEMM2, the tile's pool metadata) arrive by LDS DMA (global_load_lds) into one of N LDS stages (three;
-// four for MXFP4 weights at BLOCK_M 128, whose stages are smaller).
+// GEMM2, the tile's pool metadata) arrive by LDS DMA (global_load_lds) into one of N = 3 LDS stages.
 // The persistent work-group walks its (tile, K step) sequence as one stream.  Step s computes from
 // registers that were read from LDS during step s-1; half-way through, it waits until stage s+1 has
 // landed (vmcnt lets the N-2 youngest DMA groups stay in flight), barriers, refills its own stage with
@@ -45,11 +44,10 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kWaves = 8;         // waves per work-group, 2 per SIMD
-// LDS stages of the load pipeline (steps in flight = stages - 1).  FP8 stages (48 or 40 KB) fit three
-// times in the 160 KB of LDS.  MXFP4's halved weight chunk leaves room for more: a fourth stage (146 KB)
-// took the prefill-shaped MXFP4 layer from 1.80 to 1.78 ms; at BLOCK_M 64 (decode), five stages (141 KB)
-// were no faster than three, so that launch keeps three.
-constexpr int stages_of(int BM, bool fp4) { return fp4 && BM == 128 ? 4 : 3; }
+// LDS stages of the load pipeline (steps in flight = stages - 1); the pipeline code below holds for any
+// count.  FP8 stages (48 or 40 KB) fit three times in the 160 KB of LDS.  MXFP4's smaller stages would
+// allow four (BLOCK_M 128) or five (BLOCK_M 64), which measured no faster in same-box A/B runs.
+constexpr int stages_of(int /*BM*/, bool /*fp4*/) { return 3; }
 
 // MXFP4 weight fragment (16 rows x 128 K as e2m1, 16 bytes per lane) times an FP8 token fragment; the
 // weight rows' UE8M0 exponents come in through the MFMA's A-scale operand (byte 0 of `sa`, one per lane:
@@ -396,14 +394,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t fill_total = (uint32_t)nblocks * FillUnits<BM>::per_block;
     if constexpr (kFill) fill_pool<BM>(p, nblocks, lane);
-    // Full rounds of G tiles go by `logical`; the tiles of a partial last round by the raw work-group
-    // index, which spreads them over all eight XCDs (by `logical` they would all fall on the first few).
-    const int full = ntiles / G;
-    const int my_tiles = full + ((int)blockIdx.x < ntiles - full * G ? 1 : 0);
-    if (my_tiles == 0) {
+    if (logical >= ntiles) {
         if constexpr (kFill) sched_exit(p, nblocks, tid);
         return;
     }
+    const int my_tiles = (ntiles - 1 - logical) / G + 1;
     const int nsteps = my_tiles * KB;
 
     // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
@@ -418,7 +413,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     // every block of one expert: the blocks' A chunks and the n tiles' W chunks are shared through
     // that XCD's L2, each W tile is fetched by one or two XCDs and each A block about NT/4 times.
     auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
-        const int t = j < full ? logical + j * G : full * G + (int)blockIdx.x;
+        const int t = logical + j * G;
         const int vb = t / NT;
         int lo = 0, hi = nseg;              // the expert with off[le] <= vb < off[le+1]
         while (hi - lo > 1) {
