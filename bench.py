@@ -5,8 +5,9 @@
 One step = one mega_moe_forward (routing, pool fill, GEMM1 + SwiGLU + requant, GEMM2 + scatter,
 combine) over one resident batch of seeded synthetic inputs.  The timed region brackets exactly
 `steps` forwards with a device synchronisation on both sides; inputs and weights are already in HBM.
-Per-stage times come from HIP events the library records on the forward's stream inside the timed
-region.  Prints one JSON line.
+The per-stage times (and the roofline's kernel time) come from a second timed pass of `steps` forwards
+with HIP events the library records around each stage on the forward's stream; the headline pass has no
+events inside it.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -81,7 +82,8 @@ def cpu_baseline(shape, inp_gpu, n_experts: int):
                          experts=list(range(n_experts)))
     dt = time.perf_counter() - t0
     rows = int(out["route"].recv_tot[:n_experts].sum())
-    return {"value": rows / dt, "unit": "routed tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": rows / dt, "unit": "routed tokens/s", "cores": threads, "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{shape.name} workload: routing and pool fill of all {int(out['route'].recv_tot.sum())} "
                       f"routed rows, FFN + combine of local experts 0..{n_experts - 1} ({rows} rows), "
                       f"numpy fp64, {dt:.1f} s"}
@@ -162,6 +164,7 @@ def main():
         raise SystemExit(f"device status {status:#x} after warmup")
     recv_tot = moe.region("recv_tot", torch.int32, (shape.num_local_experts,)).cpu()
     R = int(recv_tot.sum())
+    rows_per_expert = {"max": int(recv_tot.max()), "mean": R / shape.num_local_experts, "min": int(recv_tot.min())}
     N = sum(inp["tokens_per_shard"])
 
     graph = None
@@ -173,9 +176,7 @@ def main():
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
-        stage_ms = None
-    else:
-        mm.mega_moe_set_timing(moe.h, True)
+    # the headline: exactly `steps` forwards between two events, with no per-stage events inside
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -188,17 +189,19 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
-    if graph is None:
-        stage_ms, nt = mm.mega_moe_stage_times(moe.h, with_count=True)
-        mm.mega_moe_set_timing(moe.h, False)
-        assert nt == args.steps
-    else:
-        # per-stage times from an eager timed pass (the graph replays the same kernels)
-        mm.mega_moe_set_timing(moe.h, True)
-        for _ in range(min(args.steps, 10)):
-            moe(inp, y=y)
-        stage_ms = mm.mega_moe_stage_times(moe.h)
-        mm.mega_moe_set_timing(moe.h, False)
+    # per-stage times (and the roofline's kernel time) from a second timed pass of `steps` eager forwards,
+    # with HIP events recorded by the library around each stage on the forward's stream
+    mm.mega_moe_set_timing(moe.h, True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        moe(inp, y=y)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    stage_ms, nt = mm.mega_moe_stage_times(moe.h, with_count=True)
+    mm.mega_moe_set_timing(moe.h, False)
+    assert nt == args.steps
+    ms_staged = t0.elapsed_time(t1) / args.steps
     ms = ms_total / args.steps
     status = moe.status()
     if status:
@@ -232,7 +235,8 @@ def main():
                        ", weights MXFP4 (e2m1, UE8M0 per 32 K)" if shape.weight_format == "mxfp4" else "") + (
                        f", plus a shared expert on shard {shape.local_rank}'s {shared_rows} tokens"
                        if shape.num_shared_experts else ""), "routed_rows": R, "tokens": N,
-                   "parallelism": "one GPU's EP share, source ranks emulated as shards"},
+                   "parallelism": "one GPU's EP share, source ranks emulated as shards",
+                   "routed_rows_per_local_expert": rows_per_expert},
         "gemm_pct_fp8_peak": 100.0 * gemm_tflops / FP8_PEAK_TFLOPS,
         "gemm_tflops": gemm_tflops,
         "roofline": {"bound": "mfma",
@@ -245,6 +249,7 @@ def main():
         "schedule": ("fill inside gemm1" if fused else "stream-ordered fill kernel") +
                     (", forward replayed from a HIP graph" if graph is not None else ""),
         "stages_ms": st,
+        "ms_per_step_with_stage_events": ms_staged,
         "stages": {
             "route": {"GB/s": gbs(w["route_bytes"], st["route"])},
             "fill": fill_stage,

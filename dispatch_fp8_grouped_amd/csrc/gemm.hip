@@ -158,23 +158,6 @@ __device__ __forceinline__ void wait_stage_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt immediate");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-// As wait_stage_barrier, allowing N1 outstanding operations when `wide` is set (wave-uniform) and N0
-// otherwise.  A wave's vector-memory counter counts down in issue order, global stores included (an
-// LDS DMA followed by younger stores is never reported done out of order), so when a tile's epilogue
-// stores were issued after the stage being waited for, those stores may stay in flight.
-template <int N0, int N1>
-__device__ __forceinline__ void wait_stage_barrier_sel(bool wide) {
-    static_assert(N0 >= 0 && N1 >= N0 && N1 < 64, "vmcnt immediate");
-    asm volatile("s_cmp_eq_u32 %0, 0\n\t"
-                 "s_cbranch_scc1 1f\n\t"
-                 "s_waitcnt vmcnt(%2) lgkmcnt(0)\n\t"
-                 "s_branch 2f\n"
-                 "1:\n\t"
-                 "s_waitcnt vmcnt(%1) lgkmcnt(0)\n"
-                 "2:\n\t"
-                 "s_barrier"
-                 :: "s"(__builtin_amdgcn_readfirstlane((int)wide)), "n"(N0), "n"(N1) : "memory", "scc");
-}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -185,13 +168,13 @@ __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)
 // order: per block, BM/8 units of 8 rows (codes), then BM/64 units of 64 rows (scales, written
 // block-major as whole 256-byte lines).  A wave claims a unit with one atomic (the next claim is issued
 // before the copy, so its latency hides under it), copies the unit, makes its stores visible device-wide
-// (release fence) and only then counts it in its block's arrival word and in the done word.  A unit is
-// claimed only by a running wave and nothing in a unit waits, so every wait on an arrival word ends,
-// whatever order the work-groups are dispatched in and whether or not they all fit on the GPU at once.
-// On MI355X this schedule is slower than a separate fill kernel before GEMM1 (prefill layer 2.42 vs
-// 1.97 ms): every published unit costs a device-scope L2 writeback, the polls are device-scope
-// acquires, and 8 waves per CU keep fewer rows in flight than the fill kernel's 32.  It is selected by
-// MEGA_MOE_FLAG_FILL_IN_GEMM1.
+// (release fence) and only then counts it in its block's arrival word.  Each tile waits for its own
+// block's count when its first K step is issued, so a tile whose block is complete starts while other
+// blocks are still being pulled.  A unit is claimed only by a running wave and nothing in a unit waits,
+// so every wait on an arrival word ends, whatever order the work-groups are dispatched in and whether or
+// not they all fit on the GPU at once.  It is selected by MEGA_MOE_FLAG_FILL_IN_GEMM1; on one GPU the
+// separate fill kernel is faster (every published unit costs a device-scope L2 writeback and the polls
+// are device-scope acquires), so it is not the default.
 constexpr int kFillRows = 8;                   // rows per code unit
 constexpr long long kSpinTicks = 200000000;    // ~2 s of the 100 MHz constant clock
 
@@ -289,10 +272,7 @@ __device__ __forceinline__ void fill_pool(const Params& p, int nblocks, int lane
         if (v < U::rows) fill_code_unit<BM>(p, b * BM + v * kFillRows, lane);
         else fill_scale_unit<BM>(p, b * BM + (v - U::rows) * 64, lane);
         __threadfence();        // the unit's stores are visible device-wide before it is counted
-        if (lane == 0) {
-            atomicAdd(p.sched + kSchedArrival + b, 1u);
-            atomicAdd(p.sched + kSchedDone, 1u);
-        }
+        if (lane == 0) atomicAdd(p.sched + kSchedArrival + b, 1u);
         u = next;
     }
 }
@@ -392,7 +372,6 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const int ntiles = nblocks * NT;
     const int G = gridDim.x;                    // a multiple of 8
     const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    const uint32_t fill_total = (uint32_t)nblocks * FillUnits<BM>::per_block;
     if constexpr (kFill) fill_pool<BM>(p, nblocks, lane);
     if (logical >= ntiles) {
         if constexpr (kFill) sched_exit(p, nblocks, tid);
@@ -483,6 +462,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     auto set_issue_tile = [&]() __attribute__((always_inline)) {
         int b, nt, le;
         tile_of(ij, b, nt, le);
+        // the page's per-block arrival check: the tile's pool block is complete before its first load
+        if constexpr (kFill) {
+            const uint32_t* arrival = p.sched + kSchedArrival + b;
+            if (__builtin_expect(sched_load(arrival) < FillUnits<BM>::per_block, 0))
+                spin_until(p, arrival, FillUnits<BM>::per_block, lane);
+        }
         const size_t row0 = (size_t)b * BM;
         if constexpr (kRotate) {
             const int jb = __builtin_amdgcn_readfirstlane(b - sOff[le]);    // block within its expert
@@ -619,7 +604,6 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
     int cj = 0, ckb = 0;      // compute side: tile and K step
-    bool epi_prev = false;    // the previous step ended a tile (its epilogue stores may be in flight)
 
     auto epilogue = [&](const Frags& f) __attribute__((always_inline)) {
         // lane holds acc[a][t][i]: weight row wr - rr + wrow(a) + 4g + i, token wm*BM/2 + 16t + rr
@@ -722,8 +706,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 
     // Promotion of MFMA k runs kLag MFMAs after it was issued (a ring of kRing products), so the
     // VALU never waits on the matrix core; the last kLag promotions of a step run at the start of
-    // the next one, with the previous step's factors.
-    constexpr int kLag = 3, kRing = 8;
+    // the next one, with the previous step's factors.  The launch that also pulls the pool keeps a
+    // ring of 4 and a lag of 2: its per-tile arrival check inside the loop needs the registers.
+    constexpr int kLag = kFill ? 2 : 3, kRing = kFill ? 4 : 8;
     static_assert(NMF % kRing == 0 && kLag < kRing && kLag <= NMF / 2, "promotion ring");
     v4f P[kRing];
     Frags F[2];
@@ -751,11 +736,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             if (i == 0) load_tail(fc, bufc);
             if (i == NMF / 2) {
                 __builtin_amdgcn_sched_barrier(0);
-                // stage s+1; when step s-1 ended a tile, its epilogue stores are younger than that
-                // stage's DMA and may stay in flight (GEMM2; GEMM1's few stores are cheaper to drain
-                // than the selection)
-                if constexpr (kGemm1) wait_stage_barrier<kInFlight>();
-                else wait_stage_barrier_sel<kInFlight, kInFlight + kEpiStores>(epi_prev);
+                // stage s+1: at most the kInFlight DMA operations of the younger stages may remain.
+                // That holds whatever order stores complete in, as long as loads complete in order
+                // among themselves; a tile's epilogue stores in between only add to the count.
+                wait_stage_barrier<kInFlight>();
                 __builtin_amdgcn_sched_barrier(0);
                 issue_dma(ic<buf>{});
                 load_head(fn, ic<(buf + 1) % kStages>{});
@@ -776,7 +760,6 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
             for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(acc[a][t]));
         issue_advance();
-        epi_prev = false;
         if (++ckb == KB) {
 #pragma unroll
             for (int k = NMF - kLag; k < NMF; ++k) {
@@ -788,7 +771,6 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
                 for (int t = 0; t < TM; ++t) fc.sc[j][t] = 0.f;
             epilogue(fc);
-            epi_prev = true;
             ckb = 0;
             ++cj;
         }
@@ -800,17 +782,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     for (int j = 0; j < NSW; ++j)
 #pragma unroll
         for (int t = 0; t < TM; ++t) F[1].sc[j][t] = 0.f;
-    if constexpr (kFill) {
-        // the page's per-block arrival check: the first tile's pool block is complete before its first
-        // load
-        int b0, nt0, le0;
-        tile_of(0, b0, nt0, le0);
-        spin_until(p, p.sched + kSchedArrival + b0, FillUnits<BM>::per_block, lane);
-    }
     issue_dma(ic<0>{});
-    // every other block before anything else is loaded: the fill's last units land while the first
-    // step's operands are in flight, and the tile loop itself needs no check
-    if constexpr (kFill) spin_until(p, p.sched + kSchedDone, fill_total, lane);
     issue_advance();
     // the other stages of the prologue
     auto prologue = [&](auto self, auto ic_j) __attribute__((always_inline)) {

@@ -136,6 +136,144 @@ int32_t fold_times(mega_moe_handle* h, int k) {
     return MEGA_MOE_OK;
 }
 
+
+// Caller pointers of one forward.
+struct ForwardArgs {
+    const int32_t* tps;
+    const void* x;
+    const float* x_sf;
+    const int64_t* topk_idx;
+    const float* topk_weights;
+    const void* w1;
+    const float* w1_sf;
+    const void* w2;
+    const float* w2_sf;
+    void* y;
+    int32_t* cum;
+};
+
+// The selected stages of one forward over the workspace `w` (layout L) on the current device.  `h`
+// (nullable) supplies the stage-timing events.
+int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t* w, int num_cus, uint32_t stages,
+                    const ForwardArgs& a, hipStream_t st, mega_moe_handle* h) {
+    if (!a.tps) return MEGA_MOE_ERR_INVALID_ARG;
+    if (stages == 0 || (stages & ~MEGA_MOE_STAGE_ALL)) return MEGA_MOE_ERR_INVALID_ARG;
+    const bool route = stages & MEGA_MOE_STAGE_ROUTE, fill = stages & MEGA_MOE_STAGE_FILL;
+    const bool g1 = stages & MEGA_MOE_STAGE_GEMM1, g2 = stages & MEGA_MOE_STAGE_GEMM2;
+    const bool comb = stages & MEGA_MOE_STAGE_COMBINE;
+    // pointers each selected stage reads or writes
+    auto need = [](bool used, const void* ptr) { return !used || (ptr && aligned16(ptr)); };
+    if (!need(route || comb, a.topk_idx) || !need(fill, a.x) || !need(fill, a.x_sf) || !need(g1, a.w1) ||
+        !need(g1, a.w1_sf) || !need(g2, a.w2) || !need(g2, a.w2_sf) || !need(comb, a.topk_weights) ||
+        !need(comb, a.y))
+        return MEGA_MOE_ERR_INVALID_ARG;
+    if (a.cum && ((uintptr_t)a.cum & 3u)) return MEGA_MOE_ERR_INVALID_ARG;
+
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.S = c.num_shards;
+    p.T_max = c.max_tokens_per_shard;
+    p.H = c.hidden;
+    p.I = c.intermediate;
+    p.E = c.num_experts;
+    p.El = c.num_local_experts;
+    p.nsh = c.num_shared_experts;
+    p.own = c.local_rank;
+    p.wfmt = c.weight_format;
+    p.lo = c.local_rank * c.num_local_experts;
+    p.K = c.topk;
+    p.BM = L.block_m;
+    p.chunks = L.route_chunks;
+    p.max_blocks = L.max_pool_blocks;
+    p.flags = c.flags;
+    for (int s = 0; s < c.num_shards; ++s) {
+        const int32_t t = a.tps[s];
+        if (t < 0) return MEGA_MOE_ERR_INVALID_ARG;
+        if (t > c.max_tokens_per_shard) return MEGA_MOE_ERR_TOO_MANY_TOKENS;
+        p.tps[s] = t;
+    }
+    p.status = reinterpret_cast<uint32_t*>(w + L.status);
+    p.chunk_hist = reinterpret_cast<int*>(w + L.chunk_hist);
+    p.chunk_base = reinterpret_cast<int*>(w + L.chunk_base);
+    p.send = reinterpret_cast<int*>(w + L.send);
+    p.recv = reinterpret_cast<int*>(w + L.recv);
+    p.recv_tot = reinterpret_cast<int*>(w + L.recv_tot);
+    p.pool_off = reinterpret_cast<int*>(w + L.pool_off);
+    p.block_expert = reinterpret_cast<int*>(w + L.block_expert);
+    p.block_index = reinterpret_cast<int*>(w + L.block_index);
+    p.table = reinterpret_cast<int*>(w + L.table);
+    p.pool_x = w + L.pool_x;
+    p.pool_sf = reinterpret_cast<float*>(w + L.pool_sf);
+    p.pool_meta = reinterpret_cast<uint32_t*>(w + L.pool_meta);
+    p.pool_dst = reinterpret_cast<uint32_t*>(w + L.pool_dst);
+    p.l2_x = w + L.l2_x;
+    p.l2_sf = reinterpret_cast<float*>(w + L.l2_sf);
+    p.comb = reinterpret_cast<uint16_t*>(w + L.comb);
+    p.gemm1_out = L.gemm1_out ? reinterpret_cast<float*>(w + L.gemm1_out) : nullptr;
+    p.sched = reinterpret_cast<uint32_t*>(w + L.sched);
+    p.x = static_cast<const uint8_t*>(a.x);
+    p.x_sf = a.x_sf;
+    p.topk_idx = a.topk_idx;
+    p.topk_w = a.topk_weights;
+    p.w1 = static_cast<const uint8_t*>(a.w1);
+    p.w1_sf = a.w1_sf;
+    p.w2 = static_cast<const uint8_t*>(a.w2);
+    p.w2_sf = a.w2_sf;
+    p.y = static_cast<uint16_t*>(a.y);
+    p.cum = a.cum;
+
+    int32_t rc = MEGA_MOE_OK;
+    // with FILL_IN_GEMM1 (and both stages selected) the fill runs inside GEMM1's launch
+    const bool fused_fill = fill && g1 && (c.flags & MEGA_MOE_FLAG_FILL_IN_GEMM1);
+    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill && !fused_fill, g1, g2, comb};
+    const bool timing = h && h->timing;
+    const int set = h ? h->next_set % kTimingSets : 0;
+    if (timing && h->pending[set] && fold_times(h, set) != MEGA_MOE_OK) rc = MEGA_MOE_ERR_HIP;
+    uint32_t ran_mask = 0;
+    auto mark = [&](int i) {
+        if (timing && !rc && hipEventRecord(h->ev[set][i], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+    };
+    if (!rc && route && (c.flags & MEGA_MOE_FLAG_DEBUG_POISON)) {
+        // every region a stage fills for a later one: a read of anything this forward did not write
+        // shows up as NaN in the output.  The fills are memsets, which a captured HIP graph must not
+        // hold: refused on a capturing stream.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+        else if (cs != hipStreamCaptureStatusNone) rc = MEGA_MOE_ERR_UNSUPPORTED;
+        const uint64_t regions[][2] = {{L.pool_x, L.pool_sf}, {L.pool_sf, L.pool_meta}, {L.l2_x, L.l2_sf},
+                                       {L.l2_sf, L.comb}};
+        for (const auto& r : regions)
+            if (!rc && hipMemsetAsync(w + r[0], 0xFF, r[1] - r[0], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+        const uint64_t comb_end = L.gemm1_out ? L.gemm1_out : L.sched;
+        if (!rc && hipMemsetAsync(w + L.comb, 0xFF, comb_end - L.comb, st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+        if (rc) return rc;
+    }
+    mark(0);
+    for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i) {
+        if (on[i] && !rc) {
+            hipError_t e = hipSuccess;
+            switch (i) {
+                case 0: e = mm::launch_route(p, st); break;
+                case 1: e = mm::launch_fill(p, num_cus, st); break;
+                case 2: e = mm::launch_gemm1(p, fused_fill, num_cus, st); break;
+                case 3: e = mm::launch_gemm2(p, num_cus, st); break;
+                default: e = mm::launch_combine(p, st); break;
+            }
+            if (e != hipSuccess) rc = MEGA_MOE_ERR_HIP;
+            ran_mask |= 1u << i;
+        }
+        mark(i + 1);
+    }
+    if (!rc && timing) {
+        h->ran[set] = ran_mask;
+        h->pending[set] = true;
+        ++h->next_set;
+    }
+    return rc;
+}
+
+
+
 }  // namespace
 
 extern "C" {
@@ -244,119 +382,12 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
                                 const void* x, const float* x_sf, const int64_t* topk_idx,
                                 const float* topk_weights, const void* w1, const float* w1_sf, const void* w2,
                                 const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream) {
-    if (!h || !tokens_per_shard) return MEGA_MOE_ERR_INVALID_ARG;
-    if (stages == 0 || (stages & ~MEGA_MOE_STAGE_ALL)) return MEGA_MOE_ERR_INVALID_ARG;
-    const mega_moe_config& c = h->cfg;
-    const bool route = stages & MEGA_MOE_STAGE_ROUTE, fill = stages & MEGA_MOE_STAGE_FILL;
-    const bool g1 = stages & MEGA_MOE_STAGE_GEMM1, g2 = stages & MEGA_MOE_STAGE_GEMM2;
-    const bool comb = stages & MEGA_MOE_STAGE_COMBINE;
-    // pointers each selected stage reads or writes
-    auto need = [](bool used, const void* ptr) { return !used || (ptr && aligned16(ptr)); };
-    if (!need(route || comb, topk_idx) || !need(fill, x) || !need(fill, x_sf) || !need(g1, w1) ||
-        !need(g1, w1_sf) || !need(g2, w2) || !need(g2, w2_sf) || !need(comb, topk_weights) || !need(comb, y))
-        return MEGA_MOE_ERR_INVALID_ARG;
-    if (cum_recv_stats && ((uintptr_t)cum_recv_stats & 3u)) return MEGA_MOE_ERR_INVALID_ARG;
-
-    Params p;
-    memset(&p, 0, sizeof(p));
-    p.S = c.num_shards;
-    p.T_max = c.max_tokens_per_shard;
-    p.H = c.hidden;
-    p.I = c.intermediate;
-    p.E = c.num_experts;
-    p.El = c.num_local_experts;
-    p.nsh = c.num_shared_experts;
-    p.own = c.local_rank;
-    p.wfmt = c.weight_format;
-    p.lo = c.local_rank * c.num_local_experts;
-    p.K = c.topk;
-    p.BM = h->lay.block_m;
-    p.chunks = h->lay.route_chunks;
-    p.max_blocks = h->lay.max_pool_blocks;
-    p.flags = c.flags;
-    for (int s = 0; s < c.num_shards; ++s) {
-        const int32_t t = tokens_per_shard[s];
-        if (t < 0) return MEGA_MOE_ERR_INVALID_ARG;
-        if (t > c.max_tokens_per_shard) return MEGA_MOE_ERR_TOO_MANY_TOKENS;
-        p.tps[s] = t;
-    }
-    const mega_moe_layout& L = h->lay;
-    uint8_t* w = h->ws;
-    p.status = reinterpret_cast<uint32_t*>(w + L.status);
-    p.chunk_hist = reinterpret_cast<int*>(w + L.chunk_hist);
-    p.chunk_base = reinterpret_cast<int*>(w + L.chunk_base);
-    p.send = reinterpret_cast<int*>(w + L.send);
-    p.recv = reinterpret_cast<int*>(w + L.recv);
-    p.recv_tot = reinterpret_cast<int*>(w + L.recv_tot);
-    p.pool_off = reinterpret_cast<int*>(w + L.pool_off);
-    p.block_expert = reinterpret_cast<int*>(w + L.block_expert);
-    p.block_index = reinterpret_cast<int*>(w + L.block_index);
-    p.table = reinterpret_cast<int*>(w + L.table);
-    p.pool_x = w + L.pool_x;
-    p.pool_sf = reinterpret_cast<float*>(w + L.pool_sf);
-    p.pool_meta = reinterpret_cast<uint32_t*>(w + L.pool_meta);
-    p.pool_dst = reinterpret_cast<uint32_t*>(w + L.pool_dst);
-    p.l2_x = w + L.l2_x;
-    p.l2_sf = reinterpret_cast<float*>(w + L.l2_sf);
-    p.comb = reinterpret_cast<uint16_t*>(w + L.comb);
-    p.gemm1_out = L.gemm1_out ? reinterpret_cast<float*>(w + L.gemm1_out) : nullptr;
-    p.sched = reinterpret_cast<uint32_t*>(w + L.sched);
-    p.x = static_cast<const uint8_t*>(x);
-    p.x_sf = x_sf;
-    p.topk_idx = topk_idx;
-    p.topk_w = topk_weights;
-    p.w1 = static_cast<const uint8_t*>(w1);
-    p.w1_sf = w1_sf;
-    p.w2 = static_cast<const uint8_t*>(w2);
-    p.w2_sf = w2_sf;
-    p.y = static_cast<uint16_t*>(y);
-    p.cum = cum_recv_stats;
-
+    if (!h) return MEGA_MOE_ERR_INVALID_ARG;
+    const ForwardArgs a{tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y, cum_recv_stats};
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return MEGA_MOE_ERR_HIP;
     if (dev != h->device && hipSetDevice(h->device) != hipSuccess) return MEGA_MOE_ERR_HIP;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int32_t rc = MEGA_MOE_OK;
-    // with FILL_IN_GEMM1 (and both stages selected) the fill runs inside GEMM1's launch
-    const bool fused_fill = fill && g1 && (c.flags & MEGA_MOE_FLAG_FILL_IN_GEMM1);
-    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill && !fused_fill, g1, g2, comb};
-    const int set = h->next_set % kTimingSets;
-    if (h->timing && h->pending[set] && fold_times(h, set) != MEGA_MOE_OK) rc = MEGA_MOE_ERR_HIP;
-    uint32_t ran_mask = 0;
-    auto mark = [&](int i) {
-        if (h->timing && !rc && hipEventRecord(h->ev[set][i], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
-    };
-    if (!rc && route && (c.flags & MEGA_MOE_FLAG_DEBUG_POISON)) {
-        // every region a stage fills for a later one: a read of anything this forward did not write
-        // shows up as NaN in the output
-        const uint64_t regions[][2] = {{L.pool_x, L.pool_sf}, {L.pool_sf, L.pool_meta}, {L.l2_x, L.l2_sf},
-                                       {L.l2_sf, L.comb}};
-        for (const auto& r : regions)
-            if (!rc && hipMemsetAsync(w + r[0], 0xFF, r[1] - r[0], st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
-        const uint64_t comb_end = L.gemm1_out ? L.gemm1_out : L.sched;
-        if (!rc && hipMemsetAsync(w + L.comb, 0xFF, comb_end - L.comb, st) != hipSuccess) rc = MEGA_MOE_ERR_HIP;
-    }
-    mark(0);
-    for (int i = 0; i < MEGA_MOE_NUM_STAGES; ++i) {
-        if (on[i] && !rc) {
-            hipError_t e = hipSuccess;
-            switch (i) {
-                case 0: e = mm::launch_route(p, st); break;
-                case 1: e = mm::launch_fill(p, h->num_cus, st); break;
-                case 2: e = mm::launch_gemm1(p, fused_fill, h->num_cus, st); break;
-                case 3: e = mm::launch_gemm2(p, h->num_cus, st); break;
-                default: e = mm::launch_combine(p, st); break;
-            }
-            if (e != hipSuccess) rc = MEGA_MOE_ERR_HIP;
-            ran_mask |= 1u << i;
-        }
-        mark(i + 1);
-    }
-    if (!rc && h->timing) {
-        h->ran[set] = ran_mask;
-        h->pending[set] = true;
-        ++h->next_set;
-    }
+    const int32_t rc = run_forward(h->cfg, h->lay, h->ws, h->num_cus, stages, a, static_cast<hipStream_t>(stream), h);
     if (dev != h->device) (void)hipSetDevice(dev);
     return rc;
 }
@@ -367,6 +398,7 @@ int32_t mega_moe_forward(mega_moe_handle* h, const int32_t* tokens_per_shard, co
     return mega_moe_forward_stages(h, MEGA_MOE_STAGE_ALL, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1,
                                    w1_sf, w2, w2_sf, y, cum_recv_stats, stream);
 }
+
 
 int32_t mega_moe_query_layout(const mega_moe_handle* h, mega_moe_layout* out) {
     if (!h || !out) return MEGA_MOE_ERR_INVALID_ARG;

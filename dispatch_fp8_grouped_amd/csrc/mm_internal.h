@@ -14,7 +14,6 @@ constexpr int kBN = 256;               // GEMM weight rows per tile
 constexpr uint32_t kMetaPad = 0xFFFFFFFFu;
 // Schedule words of the fill-inside-GEMM1 launch (workspace region `sched`, zero between forwards)
 constexpr int kSchedClaim = 0;         // next fill unit to claim
-constexpr int kSchedDone = 1;          // fill units completed
 constexpr int kSchedExit = 2;          // work-groups that have finished
 constexpr int kSchedArrival = 64;      // [kSchedArrival + b]: completed fill units of pool block b
 

@@ -301,7 +301,19 @@ __global__ __launch_bounds__(64) void route_table_kernel(Params p) {
         meta[2] = (uint32_t)k;
         p.pool_dst[row] = (uint32_t)(((size_t)k * p.S + s) * p.T_max + t);
     }
-    if (overflow) atomicOr(p.status, MEGA_MOE_STATUS_SLOT_OVERFLOW);
+    // An entry that found no slot is dropped, as the oracle drops it: GEMM2 never writes its combine row,
+    // so that row is zeroed here and the combine adds nothing for the entry.
+    if (overflow) {
+#pragma unroll
+        for (int r = 0; r < kPerLane; ++r) {
+            if (le_of[r] < 0 || slot_of[r] < p.T_max) continue;
+            const int f = (int)(f0 + r * 64 + lane);
+            const int t = f / p.K, k = f - t * p.K;
+            uint4* row = reinterpret_cast<uint4*>(p.comb + (((size_t)k * p.S + s) * p.T_max + t) * p.H);
+            for (int c = 0; c < (p.H >> 3); ++c) row[c] = uint4{0u, 0u, 0u, 0u};
+        }
+        atomicOr(p.status, MEGA_MOE_STATUS_SLOT_OVERFLOW);
+    }
     if (bad) atomicOr(p.status, MEGA_MOE_STATUS_BAD_LAYOUT);
 }
 

@@ -49,6 +49,7 @@ extern "C" {
 #define MEGA_MOE_ERR_WORKSPACE_TOO_SMALL (-4)  /* workspace_bytes below mega_moe_workspace_bytes() */
 #define MEGA_MOE_ERR_HIP (-5)                  /* a HIP runtime call failed */
 
+
 /* Device status bits (latched in the workspace, read by mega_moe_status). */
 #define MEGA_MOE_STATUS_BAD_EXPERT_ID 0x1u     /* some topk_idx entry was >= E; that entry was skipped */
 #define MEGA_MOE_STATUS_SLOT_OVERFLOW 0x2u     /* some (expert, shard) needed more than T_max slots */
@@ -153,14 +154,16 @@ typedef struct mega_moe_layout {
                               /* spare row that takes GEMM2's padding rows                        */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
     uint64_t sched;           /* uint32 [64 + max_pool_blocks]: FILL_IN_GEMM1 schedule: [0] next     */
-                              /*   fill unit to claim, [1] units done, [2] exit ticket, [64 + b]   */
+                              /*   fill unit to claim, [2] exit ticket, [64 + b]                  */
                               /*   units of pool block b done; all zero between forwards            */
     uint64_t total;           /* bytes needed                                                     */
 } mega_moe_layout;
 
 typedef struct mega_moe_handle mega_moe_handle;
 
-/* Bytes of device workspace the config needs (host-only arithmetic; no GPU call).
+/* Bytes of device workspace the config needs (host-only arithmetic; no GPU call).  The pages' extension
+ * is asked the same way for the size of its buffer before the caller allocates it and hands it over
+ * ("DeepGEMM Mega MoE symmetric memory deep analysis", 5.1 and 10.1).
  * Errors: INVALID_ARG (null pointer), UNSUPPORTED (config outside the limits above). */
 int32_t mega_moe_workspace_bytes(const mega_moe_config* cfg, uint64_t* bytes_out /* host */);
 
@@ -240,11 +243,13 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
                                 const float* topk_weights, const void* w1, const float* w1_sf, const void* w2,
                                 const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream);
 
-/* Region offsets of the handle's workspace.  Errors: INVALID_ARG. */
+/* Region offsets of the handle's workspace (this library's own call, for tests and tools that read or
+ * place intermediate data; the pages have no counterpart).  Errors: INVALID_ARG. */
 int32_t mega_moe_query_layout(const mega_moe_handle* h, mega_moe_layout* out /* host */);
 
-/* Synchronise `stream`, read and clear the device status word into *device_flags (host).
- * Errors: INVALID_ARG, HIP. */
+/* Synchronise `stream`, read and clear the device status word into *device_flags (host).  This library's
+ * own call (the pages define no status readback): conditions only the device sees (MEGA_MOE_STATUS_*)
+ * are latched in the workspace and read here.  Errors: INVALID_ARG, HIP. */
 int32_t mega_moe_status(mega_moe_handle* h, void* stream, uint32_t* device_flags /* host */);
 
 /* Per-stage timing.  mega_moe_set_timing(h, 1) starts (and resets) accumulation: every later forward

@@ -143,7 +143,9 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
 
     integer_codes=True draws every FP8 code from the integers -8..8 and every scale as
     one shared power of two (2^-4 for activations, 2^-6 for weights), so that every
-    product and every partial sum of the GEMMs is exact in fp32.
+    product and every partial sum of the GEMMs is exact in fp32.  With weight_format "mxfp4"
+    the weights are then any e2m1 codes with one shared UE8M0 exponent (2^-3): their values are
+    multiples of 1/2 up to 6, so the products and sums stay exact too.
     """
     S, T, H, I = shape.num_shards, shape.max_tokens_per_shard, shape.hidden, shape.intermediate
     El, K = shape.num_local_experts + shape.num_shared_experts, shape.topk
@@ -156,7 +158,20 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
         v = torch.randint(-8, 9, shape_, generator=gen, device=device).to(torch.float32)
         return v.to(torch.float8_e4m3fn).view(torch.uint8)
 
-    if integer_codes:
+    def fp4_codes(shape_):
+        # any e2m1 codes (values 0, +-0.5, ..., +-6), two per byte, the low nibble first
+        lo = torch.randint(0, 16, shape_, generator=gen, device=device)
+        hi = torch.randint(0, 16, shape_, generator=gen, device=device)
+        return (lo | (hi << 4)).to(torch.uint8)
+
+    if integer_codes and shape.weight_format == "mxfp4":
+        x = ints((S, T, H))
+        x_sf = torch.full((S, T, H // 128), 2.0 ** -4, device=device)
+        w1 = fp4_codes((El, 2 * I, H // 2))
+        w1_sf = torch.full((El, 2 * I, H // 32), 127 - 3, dtype=torch.uint8, device=device)   # 2^-3
+        w2 = fp4_codes((El, H, I // 2))
+        w2_sf = torch.full((El, H, I // 32), 127 - 3, dtype=torch.uint8, device=device)
+    elif integer_codes:
         x = ints((S, T, H))
         x_sf = torch.full((S, T, H // 128), 2.0 ** -4, device=device)
         w1 = ints((El, 2 * I, H))

@@ -34,4 +34,4 @@ from .fp8 import (e4m3fn_decode, e4m3fn_encode, bf16_round, bf16_bits)  # noqa: 
 from .fp4 import (e2m1_decode, e8m0_decode, unpack_fp4, dequant_mx)  # noqa: F401
 from .layer import (route, pool_offsets, rr_inverse, rr_position, rr_sequence,  # noqa: F401
                     fill_pool, dequant_rows, dequant_blocks, expert_ffn_rows, swiglu,
-                    requant_rows, forward, direct_token, ffn_dequantised, RouteResult)
+                    requant_rows, forward, direct_token, ffn_dequantised, dequant_weight, RouteResult)

@@ -177,3 +177,4 @@ def test_pack_scales_argument_checks():
     assert lib.mega_moe_pack_scales(ctypes.byref(fp8), a, a, a, a, None) == mm.ERR_INVALID_ARG
     assert lib.mega_moe_pack_scales(ctypes.byref(mx), None, a, a, a, None) == mm.ERR_INVALID_ARG
     assert lib.mega_moe_pack_scales(ctypes.byref(mx), a, ctypes.c_void_p(4098), a, a, None) == mm.ERR_INVALID_ARG
+

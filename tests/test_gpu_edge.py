@@ -135,11 +135,16 @@ def test_slot_overflow_status_and_clamped_layout():
     sh = MoEShape("dup", 1, 4, 256, 128, 2, 2, 2, 64, seed=24)
     inp = make_inputs(sh)
     inp["topk_idx"][:] = 0               # the same expert twice per token: 8 entries, 4 slots
-    run = Run(sh, inputs=inp)
+    # poisoned workspace: a combine row the forward never wrote would read as NaN
+    run = Run(sh, inputs=inp, flags=mm.FLAG_DEBUG_POISON)
     assert run.status & mm.STATUS_SLOT_OVERFLOW
     n = inputs_np(run)
     rt, _ = check_layout(run, n)
     assert rt.recv[0, 0] == 4
+    # the dropped entries add nothing to y, as in the oracle (their combine rows are never computed)
+    ref = oracle.forward(n, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m)
+    assert ref["route"].slot_overflow
+    _whole(run, n)
     run.close()
 
 
@@ -498,4 +503,28 @@ def test_empty_forward(case):
     n = to_numpy(full)
     ref = oracle.forward(n, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m)
     tol_check(y2.to(torch.float64).cpu().numpy(), ref["y"], case)
+    moe.close()
+
+
+def test_poison_flag_refused_under_graph_capture():
+    """DEBUG_POISON fills the workspace with memsets, which a captured HIP graph must not hold: a forward
+    with the flag on a capturing stream returns UNSUPPORTED before it records anything."""
+    print("[case] poison under capture", flush=True)
+    sh = SHAPES["tiny"]
+    inp = on_gpu(make_inputs(sh))
+    moe = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_DEBUG_POISON)
+    moe(inp)                                  # eager: allowed (and packs the weights)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    raised = None
+    with torch.cuda.graph(g):
+        try:
+            moe(inp)
+        except mm.MegaMoEError as e:
+            raised = e
+    assert raised is not None and raised.code == mm.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    y = moe(inp)                              # and the handle still works eagerly afterwards
+    torch.cuda.synchronize()
+    assert moe.status() == 0 and torch.isfinite(y.float()).all()
     moe.close()
