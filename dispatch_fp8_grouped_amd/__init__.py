@@ -28,6 +28,8 @@ ERR_UNSUPPORTED = -2
 ERR_TOO_MANY_TOKENS = -3
 ERR_WORKSPACE_TOO_SMALL = -4
 ERR_HIP = -5
+ERR_SCRATCH_TOO_SMALL = -6
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 STATUS_BAD_EXPERT_ID = 0x1
 STATUS_SLOT_OVERFLOW = 0x2
@@ -54,7 +56,7 @@ STAGE_NAMES = ("route", "fill", "gemm1", "gemm2", "combine")
 # Exported symbols of include/mega_moe.h
 EXPORTS = ("mega_moe_workspace_bytes", "mega_moe_init", "mega_moe_pack_weights", "mega_moe_pack_scales",
            "mega_moe_forward",
-           "mega_moe_forward_stages",
+           "mega_moe_forward_stages", "mega_moe_forward_noalloc",
            "mega_moe_query_layout", "mega_moe_status", "mega_moe_set_timing", "mega_moe_stage_times",
            "mega_moe_destroy", "mega_moe_strerror")
 
@@ -108,6 +110,7 @@ def lib():
         fwd = [vp, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mega_moe_forward.argtypes = fwd
         L.mega_moe_forward_stages.argtypes = [vp, u32] + fwd[1:]
+        L.mega_moe_forward_noalloc.argtypes = [ctypes.POINTER(mega_moe_config)] + fwd[1:-1] + [vp, vp]
         L.mega_moe_query_layout.argtypes = [vp, ctypes.POINTER(mega_moe_layout)]
         L.mega_moe_status.argtypes = [vp, vp, ctypes.POINTER(u32)]
         L.mega_moe_set_timing.argtypes = [vp, i32]
@@ -203,6 +206,16 @@ def mega_moe_forward(h, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w
                                 _ptr(topk_weights), _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y),
                                 _ptr(cum_recv_stats), _stream(stream))
     _check(rc, "mega_moe_forward")
+
+
+def mega_moe_forward_noalloc(cfg: mega_moe_config, tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf,
+                             w2, w2_sf, y, cum_recv_stats=None, device_status=None, stream=None):
+    """The layer without a handle or workspace (the library's static per-GPU scratch; see the header)."""
+    rc = lib().mega_moe_forward_noalloc(ctypes.byref(cfg), _tps_array(tokens_per_shard), _ptr(x), _ptr(x_sf),
+                                        _ptr(topk_idx), _ptr(topk_weights), _ptr(w1), _ptr(w1_sf), _ptr(w2),
+                                        _ptr(w2_sf), _ptr(y), _ptr(cum_recv_stats), _ptr(device_status),
+                                        _stream(stream))
+    _check(rc, "mega_moe_forward_noalloc")
 
 
 def mega_moe_query_layout(h) -> dict:

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "mm_internal.h"
@@ -273,6 +274,31 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
 }
 
 
+// ---------------------------------------------------------------- workspace for callers that cannot allocate
+// mega_moe_forward_noalloc runs its forward over this array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy from the library's first use there until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr uint64_t kScratchBytes = MEGA_MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    uint8_t* ptr = nullptr;      // device address of this device's `scratch`
+    int num_cus = 0;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Zero n words (a kernel, not hipMemsetAsync: the call may be captured into a HIP graph).
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+// Copy the forward's status bits to the caller.
+__global__ void export_status_kernel(const uint32_t* status, uint32_t* out) {
+    if (threadIdx.x == 0) *out = status[0];
+}
 
 }  // namespace
 
@@ -286,6 +312,8 @@ const char* mega_moe_strerror(int32_t code) {
         case MEGA_MOE_ERR_TOO_MANY_TOKENS: return "tokens_per_shard exceeds max_tokens_per_shard";
         case MEGA_MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mega_moe_workspace_bytes()";
         case MEGA_MOE_ERR_HIP: return "HIP runtime error";
+        case MEGA_MOE_ERR_SCRATCH_TOO_SMALL:
+            return "configuration's workspace exceeds the static scratch of mega_moe_forward_noalloc";
         default: return "unknown error";
     }
 }
@@ -399,6 +427,51 @@ int32_t mega_moe_forward(mega_moe_handle* h, const int32_t* tokens_per_shard, co
                                    w1_sf, w2, w2_sf, y, cum_recv_stats, stream);
 }
 
+
+int32_t mega_moe_forward_noalloc(const mega_moe_config* cfg, const int32_t* tokens_per_shard, const void* x,
+                                 const float* x_sf, const int64_t* topk_idx, const float* topk_weights,
+                                 const void* w1, const float* w1_sf, const void* w2, const float* w2_sf, void* y,
+                                 int32_t* cum_recv_stats, uint32_t* device_status, void* stream) {
+    if (!cfg) return MEGA_MOE_ERR_INVALID_ARG;
+    const int32_t rc = check_config(cfg);
+    if (rc) return rc;
+    // the poison fills are memsets (not for captured graphs), and the fp32 GEMM1 output is a test aid
+    if (cfg->flags & (MEGA_MOE_FLAG_DEBUG_POISON | MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT)) return MEGA_MOE_ERR_UNSUPPORTED;
+    if (device_status && ((uintptr_t)device_status & 3u)) return MEGA_MOE_ERR_INVALID_ARG;
+    mega_moe_layout L;
+    make_layout(cfg, &L);
+    if (L.total > kScratchBytes) return MEGA_MOE_ERR_SCRATCH_TOO_SMALL;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MEGA_MOE_ERR_UNSUPPORTED;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot, dev]() {
+        void* ptr = nullptr;
+        slot.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess)
+            slot.err = hipDeviceGetAttribute(&slot.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (slot.err == hipSuccess) slot.ptr = static_cast<uint8_t*>(ptr);
+    });
+    if (slot.err != hipSuccess || !slot.ptr) return MEGA_MOE_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* w = slot.ptr;
+    // what must start at zero: the status word (latched bits) and the FILL_IN_GEMM1 schedule words; every
+    // other region is written by an earlier stage of the same forward before it is read
+    const int sched_words = (int)((L.total - L.sched) / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(w + L.status), 1);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((sched_words + 255) / 256 < 64 ? (sched_words + 255) / 256 : 64),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t*>(w + L.sched), sched_words);
+    if (hipGetLastError() != hipSuccess) return MEGA_MOE_ERR_HIP;
+    const ForwardArgs a{tokens_per_shard, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y, cum_recv_stats};
+    const int32_t frc = run_forward(*cfg, L, w, slot.num_cus, MEGA_MOE_STAGE_ALL, a, st, nullptr);
+    if (frc) return frc;
+    if (device_status) {
+        hipLaunchKernelGGL(export_status_kernel, dim3(1), dim3(64), 0, st,
+                           reinterpret_cast<const uint32_t*>(w + L.status), device_status);
+        if (hipGetLastError() != hipSuccess) return MEGA_MOE_ERR_HIP;
+    }
+    return MEGA_MOE_OK;
+}
 
 int32_t mega_moe_query_layout(const mega_moe_handle* h, mega_moe_layout* out) {
     if (!h || !out) return MEGA_MOE_ERR_INVALID_ARG;

@@ -48,7 +48,12 @@ extern "C" {
 #define MEGA_MOE_ERR_TOO_MANY_TOKENS (-3)      /* tokens_per_shard[s] > max_tokens_per_shard */
 #define MEGA_MOE_ERR_WORKSPACE_TOO_SMALL (-4)  /* workspace_bytes below mega_moe_workspace_bytes() */
 #define MEGA_MOE_ERR_HIP (-5)                  /* a HIP runtime call failed */
+#define MEGA_MOE_ERR_SCRATCH_TOO_SMALL (-6)    /* mega_moe_forward_noalloc: the config's workspace
+                                                  (mega_moe_workspace_bytes) exceeds
+                                                  MEGA_MOE_NOALLOC_SCRATCH_BYTES */
 
+/* Size of the static per-GPU scratch array behind mega_moe_forward_noalloc (256 MiB). */
+#define MEGA_MOE_NOALLOC_SCRATCH_BYTES (256ull << 20)
 
 /* Device status bits (latched in the workspace, read by mega_moe_status). */
 #define MEGA_MOE_STATUS_BAD_EXPERT_ID 0x1u     /* some topk_idx entry was >= E; that entry was skipped */
@@ -242,6 +247,24 @@ int32_t mega_moe_forward_stages(mega_moe_handle* h, uint32_t stages, const int32
                                 const void* x, const float* x_sf, const int64_t* topk_idx,
                                 const float* topk_weights, const void* w1, const float* w1_sf, const void* w2,
                                 const float* w2_sf, void* y, int32_t* cum_recv_stats, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the whole layer as mega_moe_forward, with no handle and no allocation.
+ * Its workspace is a static device array of MEGA_MOE_NOALLOC_SCRATCH_BYTES (256 MiB) that every GPU the
+ * library runs on holds from the library's first use there until the process ends; the caller passes
+ * only inputs and outputs (the same ones as mega_moe_forward, weights packed by mega_moe_pack_weights)
+ * and the config.  The forward zeroes the status word and schedule words on `stream` with a kernel (no
+ * memset), so the call may be captured into a HIP graph.
+ *   device_status  uint32 (device) or NULL: receives the forward's MEGA_MOE_STATUS_* bits.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (two streams, two host
+ * threads) race, and must be serialised by the caller.  The array keeps the last call's contents.
+ * Errors: INVALID_ARG, UNSUPPORTED (config, or the DEBUG_POISON / KEEP_GEMM1_OUTPUT flags), TOO_MANY_TOKENS,
+ * SCRATCH_TOO_SMALL (mega_moe_workspace_bytes(cfg) > MEGA_MOE_NOALLOC_SCRATCH_BYTES), HIP. */
+int32_t mega_moe_forward_noalloc(const mega_moe_config* cfg, const int32_t* tokens_per_shard /* host, [S] */,
+                                 const void* x, const float* x_sf, const int64_t* topk_idx,
+                                 const float* topk_weights, const void* w1, const float* w1_sf, const void* w2,
+                                 const float* w2_sf, void* y, int32_t* cum_recv_stats, uint32_t* device_status,
+                                 void* stream);
 
 /* Region offsets of the handle's workspace (this library's own call, for tests and tools that read or
  * place intermediate data; the pages have no counterpart).  Errors: INVALID_ARG. */

@@ -178,3 +178,20 @@ def test_pack_scales_argument_checks():
     assert lib.mega_moe_pack_scales(ctypes.byref(mx), None, a, a, a, None) == mm.ERR_INVALID_ARG
     assert lib.mega_moe_pack_scales(ctypes.byref(mx), a, ctypes.c_void_p(4098), a, a, None) == mm.ERR_INVALID_ARG
 
+
+def test_noalloc_host_checks_refuse_before_any_gpu_call():
+    """mega_moe_forward_noalloc: a config whose workspace exceeds the static scratch, and the flags whose
+    forwards would record memsets or keep test buffers, are refused by host arithmetic alone."""
+    lib = mm.lib()
+    tps = (ctypes.c_int32 * 8)(*[1] * 8)
+    nul = [None] * 11
+    big = cfg_of("prefill")
+    assert mm.mega_moe_workspace_bytes(big) > mm.NOALLOC_SCRATCH_BYTES
+    assert lib.mega_moe_forward_noalloc(ctypes.byref(big), tps, *nul, None) == mm.ERR_SCRATCH_TOO_SMALL
+    dec = cfg_of("decode")
+    assert mm.mega_moe_workspace_bytes(dec) <= mm.NOALLOC_SCRATCH_BYTES
+    for flag in (mm.FLAG_DEBUG_POISON, mm.FLAG_KEEP_GEMM1_OUTPUT):
+        c = cfg_of("decode", flags=flag)
+        assert lib.mega_moe_forward_noalloc(ctypes.byref(c), tps, *nul, None) == mm.ERR_UNSUPPORTED
+    assert lib.mega_moe_forward_noalloc(None, tps, *nul, None) == mm.ERR_INVALID_ARG
+    assert "static scratch" in mm.mega_moe_strerror(mm.ERR_SCRATCH_TOO_SMALL)
