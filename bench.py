@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--fill-in-gemm1", action="store_true",
                     help="pull the pool rows inside GEMM1's launch, GEMM1 waiting on per-block arrival counts "
                          "(default: the fill is its own kernel, stream-ordered before GEMM1)")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="run GEMM1 and GEMM2 in one persistent launch, each GEMM2 tile waiting on its pool "
+                         "block's count of finished GEMM1 n tiles (default: two stream-ordered launches)")
     ap.add_argument("--cpu-experts", type=int, default=8)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="instead of the layer, run a plain elementwise copy of this many MiB five times "
@@ -149,10 +152,11 @@ def main():
     if args.weight_format != "fp8":
         shape = shape.replace(weight_format=args.weight_format)
     # the recorded HBM counters describe the default kernel configuration only
-    default_config = (shape == SHAPES[args.workload] and not args.fill_in_gemm1)
+    default_config = (shape == SHAPES[args.workload] and not args.fill_in_gemm1 and not args.one_launch)
     torch.cuda.set_device(0)
     inp = make_inputs(shape, device="cuda")
-    moe = mm.MegaMoE.from_shape(shape, flags=mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0)
+    flags = (mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0) | (mm.FLAG_ONE_GEMM_LAUNCH if args.one_launch else 0)
+    moe = mm.MegaMoE.from_shape(shape, flags=flags)
     y = torch.empty((shape.num_shards, shape.max_tokens_per_shard, shape.hidden), dtype=torch.bfloat16,
                     device="cuda")
     stream = torch.cuda.current_stream()
@@ -211,8 +215,11 @@ def main():
     w = algorithmic(shape, R, N, shared_rows)
     st = dict(zip(mm.STAGE_NAMES, stage_ms))
     fused = st["fill"] == 0.0       # the fill ran inside GEMM1's launch and is timed with it
-    g1_tflops = w["gemm1_flop"] / (st["gemm1"] * 1e-3) / 1e12
-    g2_tflops = w["gemm2_flop"] / (st["gemm2"] * 1e-3) / 1e12
+    one = st["gemm2"] == 0.0        # GEMM2 ran inside GEMM1's launch and is timed with it
+    # the dominant kernel: GEMM1's launch (with GEMM2's flops when GEMM2 runs inside it)
+    g1_flop = w["gemm1_flop"] + (w["gemm2_flop"] if one else 0.0)
+    g1_tflops = g1_flop / (st["gemm1"] * 1e-3) / 1e12
+    g2_tflops = 0.0 if one else w["gemm2_flop"] / (st["gemm2"] * 1e-3) / 1e12
     gemm_tflops = (w["gemm1_flop"] + w["gemm2_flop"]) / ((st["gemm1"] + st["gemm2"]) * 1e-3) / 1e12
     gbs = lambda b, t: b / (t * 1e-3) / 1e9  # noqa: E731
     fill_stage = ({"schedule": "inside the gemm1 launch (per-block arrival counts); timed with gemm1"} if fused
@@ -240,13 +247,15 @@ def main():
         "gemm_pct_fp8_peak": 100.0 * gemm_tflops / FP8_PEAK_TFLOPS,
         "gemm_tflops": gemm_tflops,
         "roofline": {"bound": "mfma",
-                     "kernel": "gemm1 (" + ("pool fill + " if fused else "") + "gate_up + SwiGLU + requant)",
+                     "kernel": "gemm1 (" + ("pool fill + " if fused else "") + "gate_up + SwiGLU + requant" +
+                               (" + down GEMM + scatter, one launch" if one else "") + ")",
                      "achieved": g1_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": g1_tflops / FP8_PEAK_TFLOPS,
                      "traffic": measured_traffic(args.workload) if default_config else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic": "4*R*H*I flop per launch, R = routed rows"},
+                     "algorithmic": ("6" if one else "4") + "*R*H*I flop per launch, R = routed rows"},
         "schedule": ("fill inside gemm1" if fused else "stream-ordered fill kernel") +
+                    (", gemm2 inside gemm1's launch" if one else "") +
                     (", forward replayed from a HIP graph" if graph is not None else ""),
         "stages_ms": st,
         "ms_per_step_with_stage_events": ms_staged,
@@ -254,7 +263,8 @@ def main():
             "route": {"GB/s": gbs(w["route_bytes"], st["route"])},
             "fill": fill_stage,
             "gemm1": {"TFLOP/s": g1_tflops, "frac": g1_tflops / FP8_PEAK_TFLOPS},
-            "gemm2": {"TFLOP/s": g2_tflops, "frac": g2_tflops / FP8_PEAK_TFLOPS},
+            "gemm2": ({"schedule": "inside the gemm1 launch (per-block GEMM1 counts); timed with gemm1"} if one
+                      else {"TFLOP/s": g2_tflops, "frac": g2_tflops / FP8_PEAK_TFLOPS}),
             "combine": {"GB/s": gbs(w["combine_bytes"], st["combine"]),
                         "hbm_frac": gbs(w["combine_bytes"], st["combine"]) / HBM_PEAK_GBS},
             "weights_stream_GB/s": gbs(w["weight_bytes"], st["gemm1"] + st["gemm2"]),

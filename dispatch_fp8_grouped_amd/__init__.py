@@ -35,11 +35,13 @@ STATUS_BAD_EXPERT_ID = 0x1
 STATUS_SLOT_OVERFLOW = 0x2
 STATUS_BAD_LAYOUT = 0x4
 STATUS_TIMEOUT = 0x8
+STATUS_PLACEMENT = 0x10
 
 FLAG_KEEP_GEMM1_OUTPUT = 0x1
 FLAG_FILL_IN_GEMM1 = 0x2
 FLAG_DEBUG_FORCE_TIMEOUT = 0x4
 FLAG_DEBUG_POISON = 0x8
+FLAG_ONE_GEMM_LAUNCH = 0x10
 
 WEIGHTS_FP8 = 0
 WEIGHTS_MXFP4 = 1

@@ -149,6 +149,17 @@ __device__ __forceinline__ void dma4_lane(const void* src, const void* dst) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
 }
+// 4 bytes per active lane from base + off (base wave-uniform, off per lane) to LDS at dst + lane * 4
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, const void* dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_addr(dst)) : "memory", "m0");
+}
+// 4 bytes per active lane with the cache policy of a device-scope atomic load (sc1), for schedule words
+// that other work-groups of the launch update
+__device__ __forceinline__ void dma4_coherent(const void* src, const void* dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off sc1"
+                 :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding and its LDS reads have
 // returned, then barrier.  The compiler's __syncthreads would drain every LDS DMA in flight; this keeps
@@ -159,22 +170,28 @@ __device__ __forceinline__ void wait_stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Wait until every vector-memory access of this wave, stores included, has completed.
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 
-// ---------------------------------------------------------------- pool fill inside GEMM1
-// The pull of "Mega-MoE notes, part 2: index table and pull" (2.6), with that page's per-block arrival
-// count, done by GEMM1's own work-groups before their first tile.  Work is claimed in units, in pool
-// order: per block, BM/8 units of 8 rows (codes), then BM/64 units of 64 rows (scales, written
-// block-major as whole 256-byte lines).  A wave claims a unit with one atomic (the next claim is issued
-// before the copy, so its latency hides under it), copies the unit, makes its stores visible device-wide
-// (release fence) and only then counts it in its block's arrival word.  Each tile waits for its own
-// block's count when its first K step is issued, so a tile whose block is complete starts while other
-// blocks are still being pulled.  A unit is claimed only by a running wave and nothing in a unit waits,
-// so every wait on an arrival word ends, whatever order the work-groups are dispatched in and whether or
-// not they all fit on the GPU at once.  It is selected by MEGA_MOE_FLAG_FILL_IN_GEMM1; on one GPU the
-// separate fill kernel is faster (every published unit costs a device-scope L2 writeback and the polls
-// are device-scope acquires), so it is not the default.
+// ---------------------------------------------------------------- launches that hand data over inside
+// Two schedules let a kernel consume rows that other work-groups of the same launch produce:
+//   FILL_IN_GEMM1: GEMM1's work-groups first pull the pool rows themselves, with the per-block arrival
+//     count of "Mega-MoE notes, part 2: index table and pull" (2.6), and a GEMM1 tile waits for its own
+//     block's count before its first load;
+//   ONE_GEMM_LAUNCH: GEMM1 and GEMM2 run in one persistent launch, and a GEMM2 tile waits for the count
+//     of finished GEMM1 n tiles of its pool block ("MoE fused operators", DeepGEMM part, 2: the L2 GEMM
+//     waits per m block for its L1 n tiles).
+// Every hand-over stays inside one XCD.  The work-groups of XCD x (read from the hardware register
+// XCC_ID) own a contiguous range of pool blocks: they pull those blocks' rows, run their GEMM1 tiles and
+// then their GEMM2 tiles.  The producer's stores reach that XCD's L2 (s_waitcnt vmcnt(0)) before a
+// relaxed device-scope atomic counts them, and the consumer's loads are served by the same L2, which is
+// the coherence point of all CUs of an XCD; no L2 writeback or invalidation is needed.  A work-group
+// takes its slot (XCD, blockIdx / 8) with an atomic bit: if the hardware ever placed two work-groups in
+// one slot (dispatch not round-robin over the eight XCDs), MEGA_MOE_STATUS_PLACEMENT is latched.
+// Consumers read the count through a one-lane probe DMA issued with every K step (so the check costs
+// no pipeline drain) and fall back to bounded polls; nothing waits on work that no running wave holds.
+constexpr int kXcds = 8;
 constexpr int kFillRows = 8;                   // rows per code unit
 constexpr long long kSpinTicks = 200000000;    // ~2 s of the 100 MHz constant clock
 
@@ -183,16 +200,19 @@ struct FillUnits {
     static constexpr int rows = BM / kFillRows, scales = BM / 64, per_block = rows + scales;
 };
 
+// The XCD this wave runs on (HW_REG_XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcc_id() { return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u); }
+
 __device__ __forceinline__ uint32_t claim_unit(uint32_t* ctr, int lane) {
     uint32_t u = 0;
     if (lane == 0) u = atomicAdd(ctr, 1u);
     return __builtin_amdgcn_readfirstlane(u);
 }
 
-// device-scope acquire load of a schedule word, one per wave
-__device__ __forceinline__ uint32_t sched_load(const uint32_t* ptr) {
+// device-scope relaxed load of a schedule word, one per wave
+__device__ __forceinline__ uint32_t sched_peek(const uint32_t* ptr) {
     return __builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(const_cast<uint32_t*>(ptr), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+        __hip_atomic_load(const_cast<uint32_t*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Codes of pool rows row0 .. row0+7 (one block).  Lane l copies chunk columns l, l+64, ... of every
@@ -260,33 +280,37 @@ __device__ __forceinline__ void fill_scale_unit(const Params& p, int row0, int l
     }
 }
 
-// Claim, copy and publish fill units until none is left.
+// Pull the rows of pool blocks [blo, bhi) in units, in pool order: per block, BM/8 units of 8 rows
+// (codes), then BM/64 units of 64 rows (scales, written block-major as whole 256-byte lines).  A wave
+// claims a unit with one atomic on its XCD's counter (the next claim is issued before the copy, so its
+// latency hides under it), copies it, waits until its stores have completed and only then counts it in
+// its block's arrival word.
 template <int BM>
-__device__ __forceinline__ void fill_pool(const Params& p, int nblocks, int lane) {
+__device__ __forceinline__ void fill_blocks(const Params& p, int blo, int bhi, uint32_t* claim, int lane) {
     using U = FillUnits<BM>;
-    const uint32_t total = (uint32_t)nblocks * U::per_block;
-    uint32_t u = claim_unit(p.sched + kSchedClaim, lane);
+    const uint32_t total = (uint32_t)(bhi - blo) * U::per_block;
+    uint32_t u = claim_unit(claim, lane);
     while (u < total) {
-        const uint32_t next = claim_unit(p.sched + kSchedClaim, lane);
-        const int b = (int)(u / U::per_block), v = (int)(u % U::per_block);
+        const uint32_t next = claim_unit(claim, lane);
+        const int b = blo + (int)(u / U::per_block), v = (int)(u % U::per_block);
         if (v < U::rows) fill_code_unit<BM>(p, b * BM + v * kFillRows, lane);
         else fill_scale_unit<BM>(p, b * BM + (v - U::rows) * 64, lane);
-        __threadfence();        // the unit's stores are visible device-wide before it is counted
+        wait_all_vm();
         if (lane == 0) atomicAdd(p.sched + kSchedArrival + b, 1u);
         u = next;
     }
 }
 
-// Bounded spin (per wave) until *word reaches `target`; every poll is a device-scope acquire, so polls
-// are spaced by a sleep.  A wait longer than kSpinTicks latches TIMEOUT and gives up: never expected,
-// it keeps a broken schedule from hanging the GPU.  MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT makes every wait
-// give up as soon as the clock moves, so tests reach that path from the host.
+// Bounded spin (per wave) until *word reaches `target`; polls are spaced by a sleep.  A wait longer than
+// kSpinTicks latches TIMEOUT and gives up: never expected, it keeps a broken schedule from hanging the
+// GPU.  MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT makes every wait give up as soon as the clock moves, so tests
+// reach that path from the host.
 __device__ __forceinline__ void spin_until(const Params& p, const uint32_t* word, uint32_t target, int lane) {
     const bool force = p.flags & MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT;
-    if (!force && sched_load(word) >= target) return;
+    if (!force && sched_peek(word) >= target) return;
     const long long limit = force ? 0 : kSpinTicks;
     const long long t0 = wall_clock64();
-    while (force || sched_load(word) < target) {
+    while (force || sched_peek(word) < target) {
         if (wall_clock64() - t0 > limit) {
             if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_TIMEOUT);
             return;
@@ -295,16 +319,21 @@ __device__ __forceinline__ void spin_until(const Params& p, const uint32_t* word
     }
 }
 
-// Every work-group takes an exit ticket after its last access to the schedule words; the last one
-// returns them to zero, so every forward starts from a clean schedule.
+// Every work-group takes an exit ticket after its last access to the schedule words (its atomics have
+// completed); the last one returns them to zero, so every forward starts from a clean schedule.
 __device__ __forceinline__ void sched_exit(const Params& p, int nblocks, int tid) {
     __shared__ int sLast;
+    wait_all_vm();
     __syncthreads();
     if (tid == 0) sLast = atomicAdd(p.sched + kSchedExit, 1u) == gridDim.x - 1;
     __syncthreads();
     if (sLast) {
-        for (int i = tid; i < nblocks; i += blockDim.x) p.sched[kSchedArrival + i] = 0;
-        if (tid < kSchedArrival) p.sched[tid] = 0;
+        auto zero = [](uint32_t* w) { __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        for (int i = tid; i < nblocks; i += blockDim.x) {
+            zero(p.sched + kSchedArrival + i);
+            zero(p.sched + kSchedArrival + p.max_blocks + i);
+        }
+        if (tid < kSchedArrival) zero(p.sched + tid);
     }
 }
 
@@ -318,14 +347,74 @@ using ic = std::integral_constant<int, V>;
 #define MM_ROT_N 2
 #endif
 
-// Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.  kFill (GEMM1 only): the work-groups
-// first pull the pool rows (fill_pool) and every tile waits for its block's arrival count.  kStreamW:
-// the weight DMA carries the non-temporal hint, for launches where each weight chunk is read by one
-// tile only (about one pool block per expert, as at decode); where several blocks of an expert share a
-// weight chunk through L2 (prefill) the hint costs 11% and is not used.  kFp4: MXFP4 weights (two e2m1
-// codes per byte, 64-byte rows per K step, UE8M0 exponents per 32 K applied by the MFMA's scale operand).
-template <int BM, int NW, bool kGemm1, bool kFill, bool kStreamW, bool kFp4>
-__global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
+// LDS of a work-group.  Each array is a function-local __shared__ variable of a template that does not
+// depend on which GEMM runs, so the two phases of a launch that runs both GEMMs share it, and each
+// array keeps its own symbol (the allocator places them as separately declared arrays).
+template <int BM, int NW, bool kFp4>
+struct GemmLds {
+    static constexpr int kStages = stages_of(BM, kFp4);
+    static constexpr int WRB = kFp4 ? 64 : 128;     // weight bytes per row and K step
+    __device__ __forceinline__ static auto& sA() {
+        __shared__ __attribute__((aligned(1024))) uint8_t v[kStages][BM * 128];
+        return v;
+    }
+    __device__ __forceinline__ static auto& sB() {
+        __shared__ __attribute__((aligned(1024))) uint8_t v[kStages][256 * WRB];
+        return v;
+    }
+    // MXFP4: per stage and wave, the UE8M0 exponents of the wave's 64 weight rows (4 bytes = 4 K blocks)
+    __device__ __forceinline__ static auto& sWs() {
+        __shared__ __attribute__((aligned(16))) uint32_t v[kStages][kFp4 ? NW * 64 : 1];
+        return v;
+    }
+    // per stage and wave, 64 dwords written by one DMA: [0, BM/NW) token scales of rows
+    // wave*BM/NW + l, then the wave's two weight-block scales, then (GEMM2) the rows' scatter targets
+    __device__ __forceinline__ static auto& sSmall() {
+        __shared__ __attribute__((aligned(16))) uint32_t v[kStages][NW * 64];
+        return v;
+    }
+    // per stage and wave, the schedule word of the next tile's block (probe DMA)
+    __device__ __forceinline__ static auto& sProbe() {
+        __shared__ __attribute__((aligned(16))) uint32_t v[kStages][NW];
+        return v;
+    }
+    __device__ __forceinline__ static auto& sRed() {
+        __shared__ float v[BM][NW / 2];
+        return v;
+    }
+    __device__ __forceinline__ static auto& sOff() {
+        __shared__ int v[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
+        return v;
+    }
+};
+
+// Which pool blocks a work-group's tiles come from, and which of their tiles it takes: tiles first,
+// first + stride, ... of the blocks [blo, bhi), numbered as described at tile_of.
+struct TilePlan {
+    int blo, bhi, first, stride;
+};
+
+// The wait of a phase's tiles before their first load: none, the fill units of the tile's block, or
+// the GEMM1 n tiles of the tile's block.
+enum { kWaitNone = 0, kWaitFill = 1, kWaitGemm1 = 2 };
+
+// One GEMM over the plan's tiles.  Work-group: NW waves in a 2 x NW/2 grid over the BM x 256 tile.
+// kStreamW: the weight DMA carries the non-temporal hint, for launches where each weight chunk is read
+// by one tile only (about one pool block per expert, as at decode); where several blocks of an expert
+// share a weight chunk through L2 (prefill) the hint costs 11% and is not used.  kFp4: MXFP4 weights
+// (two e2m1 codes per byte, 64-byte rows per K step, UE8M0 exponents per 32 K applied by the MFMA's
+// scale operand).  kWait: what a tile waits for before its first load.  kPublish (GEMM1): after a
+// tile's stores have completed, count the tile in its block's GEMM1 word.
+template <int BM, int NW, bool kGemm1, bool kStreamW, bool kFp4, int kWait, bool kPublish, bool kXcd>
+__device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan, int nblocks) {
+    using Lds = GemmLds<BM, NW, kFp4>;
+    auto& sA = Lds::sA();
+    auto& sB = Lds::sB();
+    auto& sWs = Lds::sWs();
+    auto& sSmall = Lds::sSmall();
+    auto& sProbe = Lds::sProbe();
+    auto& sRed = Lds::sRed();
+    auto& sOff = Lds::sOff();
     constexpr int NWN = NW / 2;                 // compute waves along the weight (N) side
     constexpr int TM = BM / 32;                 // 16-token subtiles per wave (wave covers BM/2 tokens)
     constexpr int WROWS = 256 / NWN;            // weight rows per wave
@@ -333,11 +422,18 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int HC = WROWS / 2;               // GEMM1: output columns per wave (gate + up halves)
     constexpr int NMF = TM * WN;                // MFMAs per wave and K step
     constexpr int A_INS = BM / (8 * NW);        // 1 KB A DMA instructions per wave and step
-    constexpr int WRB = kFp4 ? 64 : 128;       // weight bytes per row and K step
+    constexpr int WRB = GemmLds<BM, NW, kFp4>::WRB;
     constexpr int B_INS = (256 * WRB / 1024) / NW;   // 1 KB B DMA instructions per wave and step
     constexpr int SA_LANES = BM / NW;           // token rows whose scale (and GEMM2 target) a wave loads
-    // per step: A and B chunks, the small DMA and (MXFP4) the wave's weight-row exponents
-    constexpr int DMA_PER_STEP = A_INS + B_INS + 1 + (kFp4 ? 1 : 0);
+    // The small DMA: a phase whose tiles do not wait loads its token scales, weight-block scales and
+    // (GEMM2) scatter targets with one instruction from per-lane addresses (kLaneSmall); a phase whose
+    // tiles wait needs those registers for its per-tile check and uses one exec-masked instruction per
+    // kind of word from wave-uniform bases instead (one more DMA per step, two more with GEMM2).
+    constexpr bool kLaneSmall = kWait == kWaitNone;
+    // per step: A and B chunks, the small DMA, (MXFP4) the wave's weight-row exponents and (kWait) the
+    // probe of the next tile's word
+    constexpr int DMA_PER_STEP = A_INS + B_INS + 1 + (kFp4 ? 1 : 0) +
+                                 (kLaneSmall ? 0 : (kFp4 ? 0 : 1) + (kGemm1 ? 0 : 1) + 1);
     // global stores every wave issues in a GEMM2 tile's epilogue: two per 16-token group
     constexpr int kEpiStores = 2 * TM;
     // K-start rotation per block within the expert and per n tile (see the issue side below); it
@@ -346,20 +442,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     constexpr int kRotJ = MM_ROT_J, kRotN = MM_ROT_N;
     static_assert(A_INS >= 1 && B_INS >= 1 && 2 * SA_LANES + 2 <= 64, "tile shape");
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
-    static_assert(kGemm1 || !kFill, "the fill feeds GEMM1 only");
-    constexpr int kStages = stages_of(BM, kFp4);
+    static_assert(kGemm1 || kWait != kWaitFill, "the fill feeds GEMM1 only");
+    static_assert(kGemm1 || !kPublish, "GEMM1 publishes its tiles");
+    constexpr int kStages = GemmLds<BM, NW, kFp4>::kStages;
     constexpr int kInFlight = (kStages - 2) * DMA_PER_STEP;   // at mid-step: the steps after the next one
     static_assert((kStages - 1) * DMA_PER_STEP + kEpiStores < 64, "vmcnt immediate");
-
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][BM * 128];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][256 * WRB];
-    // MXFP4: per stage and wave, the UE8M0 exponents of the wave's 64 weight rows (4 bytes = 4 K blocks)
-    __shared__ __attribute__((aligned(16))) uint32_t sWs[kStages][kFp4 ? NW * 64 : 1];
-    // per stage and wave, 64 dwords written by one DMA: [0, SA_LANES) token scales of rows
-    // wave*SA_LANES + l, then the wave's two weight-block scales, then (GEMM2) the rows' scatter targets
-    __shared__ __attribute__((aligned(16))) uint32_t sSmall[kStages][NW * 64];
-    __shared__ float sRed[BM][NWN];
-    __shared__ int sOff[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -368,42 +455,32 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const int Kdim = kGemm1 ? p.H : p.I;
     const int KB = Kdim >> 7;
     const int NT = kGemm1 ? (p.I >> 7) : (p.H >> 8);
-    const int nblocks = min((int)p.status[1], p.max_blocks);
-    const int ntiles = nblocks * NT;
-    const int G = gridDim.x;                    // a multiple of 8
-    const int logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    if constexpr (kFill) fill_pool<BM>(p, nblocks, lane);
-    if (logical >= ntiles) {
-        if constexpr (kFill) sched_exit(p, nblocks, tid);
-        return;
-    }
-    const int my_tiles = (ntiles - 1 - logical) / G + 1;
+    const int ntiles = (plan.bhi - plan.blo) * NT;
+    if (plan.first >= ntiles) return;
+    const int my_tiles = (ntiles - 1 - plan.first) / plan.stride + 1;
     const int nsteps = my_tiles * KB;
-
-    // expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
-    // waits on a global load of its own
     const int nseg = p.El + p.nsh;              // pool segments: routed experts, then the shared one
-    for (int i = tid; i <= nseg; i += NW * 64) sOff[i] = p.pool_off[i];
-    __syncthreads();
 
-    // Tile t -> pool block, n tile and local expert.  Tiles are numbered expert by expert (expert le
-    // owns tiles [off[le]*NT, off[le+1]*NT)), inside an expert n tile by n tile, then block by block.
-    // A run of 32 consecutive tiles (one XCD's share of a round) then covers about four n tiles of
-    // every block of one expert: the blocks' A chunks and the n tiles' W chunks are shared through
-    // that XCD's L2, each W tile is fetched by one or two XCDs and each A block about NT/4 times.
+    // Tile t of the plan -> pool block, n tile and local expert.  With c[le] = the offset of expert le
+    // clipped to the plan's blocks (relative to blo), tiles are numbered expert by expert (expert le
+    // owns tiles [c[le]*NT, c[le+1]*NT)), inside an expert n tile by n tile, then block by block.  A
+    // run of 32 consecutive tiles (one XCD's share of a round) then covers about four n tiles of every
+    // block of one expert: the blocks' A chunks and the n tiles' W chunks are shared through that
+    // XCD's L2, each W tile is fetched by one or two XCDs and each A block about NT/4 times.
+    auto clip = [&](int i) { return kXcd ? min(max(sOff[i], plan.blo), plan.bhi) - plan.blo : sOff[i]; };
     auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
-        const int t = logical + j * G;
+        const int t = plan.first + j * plan.stride;
         const int vb = t / NT;
-        int lo = 0, hi = nseg;              // the expert with off[le] <= vb < off[le+1]
+        int lo = 0, hi = nseg;              // the expert with c[le] <= vb < c[le+1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (sOff[mid] <= vb) lo = mid; else hi = mid;
+            if (clip(mid) <= vb) lo = mid; else hi = mid;
         }
         le = lo;
-        const int b0 = sOff[lo], nb = max(sOff[lo + 1] - b0, 1);
+        const int b0 = clip(lo), nb = max(clip(lo + 1) - b0, 1);
         const int u = t - b0 * NT;
         nt = u / nb;
-        b = b0 + (u - nt * nb);
+        b = plan.blo + b0 + (u - nt * nb);
         // wave-uniform by construction; the offsets come from LDS, so say so for the scalar DMA bases
         b = __builtin_amdgcn_readfirstlane(min(max(b, 0), nblocks - 1));   // inconsistent offsets only
         nt = __builtin_amdgcn_readfirstlane(min(max(nt, 0), NT - 1));
@@ -417,7 +494,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         return (kGemm1 ? p.w1 : p.w2) + ((size_t)le * NT + nt) * KB * (256 * WRB);
     };
 
-    // per-lane DMA offsets (fixed for the whole kernel)
+    // per-lane DMA offsets (fixed for the whole phase)
     uint32_t a_off[A_INS], b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -435,14 +512,28 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             b_off[i] = r * 128 + c * 16;
         }
     }
-    // lane role in the small DMA: token scale of row wave*SA_LANES + l, weight-block scale j, or
-    // (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes repeat lane 0's load
-    // (MXFP4 weights carry no 128x128 block scales: those two lanes repeat lane 0's load)
+    // The small DMA fills the wave's 64 dwords of sSmall with one exec-masked instruction per kind of
+    // word, each from a wave-uniform base: the token scales (lanes [0, SA_LANES): rows
+    // wave*SA_LANES + l), the two weight-block scales (lanes SA_LANES and SA_LANES + 1; FP8 weights) and,
+    // for GEMM2, the scatter targets of the same rows (lanes SA_LANES + 2 ..).  A lane's byte offset
+    // from its kind's base is fixed for the phase.
+    // kLaneSmall: lane role in the one small DMA (token scale of row wave*SA_LANES + l, weight-block
+    // scale j, or (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes, and with MXFP4 weights
+    // the two weight-scale lanes, repeat lane 0's load) and the bytes its address advances per K step
+    // (token scales are block-major, BM per K block; weight scales K-contiguous)
     const int sm_role = lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? (kFp4 ? 3 : 1)
                       : (!kGemm1 && lane < 2 * SA_LANES + 2) ? 2 : 3;
     const int sm_row = wave * SA_LANES + (sm_role == 0 ? lane : sm_role == 2 ? lane - SA_LANES - 2 : 0);
-    // bytes per K step: token scales are block-major (BM per K block), weight scales K-contiguous
     const uint32_t sm_inc = sm_role == 2 ? 0u : sm_role == 1 ? 4u : (uint32_t)(BM * 4);
+    const bool sc_lane = lane < SA_LANES;
+    const bool ws_lane = !kFp4 && (unsigned)(lane - SA_LANES) < 2u;
+    const bool tg_lane = !kGemm1 && (unsigned)(lane - SA_LANES - 2) < (unsigned)SA_LANES;
+    const uint32_t sm_off = ws_lane ? (kGemm1 && lane == SA_LANES + 1 ? (uint32_t)((p.I >> 7) * KB * 4) : 0u)
+                                    : (uint32_t)(wave * SA_LANES + (sc_lane ? lane : max(lane - SA_LANES - 2, 0))) * 4u;
+
+    // kWait: the words the tiles wait on (per pool block) and the count that completes a block
+    const uint32_t* wait_words = p.sched + kSchedArrival + (kWait == kWaitGemm1 ? p.max_blocks : 0);
+    const uint32_t wait_target = kWait == kWaitFill ? (uint32_t)FillUnits<BM>::per_block : (uint32_t)(p.I >> 7);
 
     // Issue side: the next step to load, tile ij, its ikb-th K step, K block ikc.  With kRotate a tile
     // walks its K blocks from a start that depends on its block and n tile, wrapping around: the
@@ -452,21 +543,33 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     int ij = 0, ikb = 0, ikc = 0;
     const uint8_t* iA;
     const uint8_t* iW;
-    const uint8_t* iSm;     // per lane
-    const uint8_t* iWs;     // per lane (MXFP4): the exponent word of this lane's weight row
+    const uint8_t* iSm;     // kLaneSmall: per lane
+    const uint8_t* iWsl;    // kLaneSmall, MXFP4: per lane, the exponent word of this lane's weight row
+    const uint8_t* iSc;     // the step's token scales (block-major: BM per K block)
+    const uint8_t* iWsc;    // (FP8) the tile's first weight-block scale of the step (K-contiguous)
+    const uint8_t* iDst;    // (GEMM2) the scatter targets of the tile's rows
+    const uint8_t* iWs;     // (MXFP4) the exponent words of the step's 256 weight rows
+    const uint32_t* iProbe = wait_words;    // kWait: the schedule word of the next tile's block
     // MXFP4: the tile row whose exponents this lane loads, fragment lane >> 4, row lane & 15 (the rows
     // the wave's weight fragments cover, in the order they are read back; 32 consecutive rows per half
     // wave, so one step's exponent load is two 128-byte runs)
     const int ws_tr = kGemm1 ? wn * 32 + ((lane >> 4) < 2 ? 0 : 128) + ((lane >> 4) & 1) * 16 + (lane & 15)
                              : wn * WROWS + (lane >> 4) * 16 + (lane & 15);
-    auto set_issue_tile = [&]() __attribute__((always_inline)) {
+    const uint32_t ws_off = (uint32_t)ws_tr * 4u;
+    // landed: the stage whose DMA landed last (-1 in the prologue)
+    auto set_issue_tile = [&](int landed) __attribute__((always_inline)) {
         int b, nt, le;
         tile_of(ij, b, nt, le);
-        // the page's per-block arrival check: the tile's pool block is complete before its first load
-        if constexpr (kFill) {
-            const uint32_t* arrival = p.sched + kSchedArrival + b;
-            if (__builtin_expect(sched_load(arrival) < FillUnits<BM>::per_block, 0))
-                spin_until(p, arrival, FillUnits<BM>::per_block, lane);
+        if constexpr (kWait != kWaitNone) {
+            // The tile's block is complete before its first load.  The probe DMA of the steps issued
+            // for the previous tile read this block's word: the stage that landed last holds its value
+            // when a tile has at least kStages steps.  Otherwise, or while incomplete, poll.
+            const bool seen = landed >= 0 && KB >= kStages &&
+                              __builtin_amdgcn_readfirstlane(sProbe[landed][wave]) >= wait_target;
+            if (__builtin_expect(!seen, 0)) spin_until(p, wait_words + b, wait_target, lane);
+            int bn = b, ntn, len;
+            if (ij + 1 < my_tiles) tile_of(ij + 1, bn, ntn, len);
+            iProbe = static_cast<const uint32_t*>(sgpr_ptr(wait_words + bn));
         }
         const size_t row0 = (size_t)b * BM;
         if constexpr (kRotate) {
@@ -477,25 +580,43 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         }
         iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b) + (size_t)ikc * BM * 128));
         iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt) + (size_t)ikc * 256 * WRB));
+        if constexpr (kLaneSmall) {
+            if constexpr (kFp4) {
+                const size_t nts = kGemm1 ? (size_t)(p.I >> 7) : (size_t)(p.H >> 8);
+                iWsl = reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf : p.w2_sf) +
+                       (((size_t)le * nts + nt) * KB + ikc) * 1024 + ws_tr * 4;
+            }
+            const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (size_t)b * KB * BM + sm_row;
+            int blk;
+            if (kGemm1) blk = lane == SA_LANES ? nt : (p.I >> 7) + nt;     // gate block, up block
+            else blk = nt * 2 + (wn * WROWS) / 128;
+            const float* wsf = (kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
+                                       : p.w2_sf + (size_t)le * (p.H >> 7) * KB) + (size_t)blk * KB;
+            const uint32_t* dst = p.pool_dst + row0 + sm_row;
+            iSm = (sm_role == 1 ? reinterpret_cast<const uint8_t*>(wsf)
+                 : sm_role == 2 ? reinterpret_cast<const uint8_t*>(dst) : reinterpret_cast<const uint8_t*>(asf)) +
+                  (size_t)ikc * sm_inc;
+            return;
+        }
         if constexpr (kFp4) {
             // packed exponents: [E_w][n tile][K block][256 rows] words, one word = the row's four 32-value blocks
             const size_t nts = kGemm1 ? (size_t)(p.I >> 7) : (size_t)(p.H >> 8);
-            iWs = reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf : p.w2_sf) +
-                  (((size_t)le * nts + nt) * KB + ikc) * 1024 + ws_tr * 4;
+            iWs = static_cast<const uint8_t*>(sgpr_ptr(reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf : p.w2_sf) +
+                                                       (((size_t)le * nts + nt) * KB + ikc) * 1024));
         }
-        const float* asf = (kGemm1 ? p.pool_sf : p.l2_sf) + (size_t)b * KB * BM + sm_row;
-        int blk;
-        if (kGemm1) blk = lane == SA_LANES ? nt : (p.I >> 7) + nt;     // gate block, up block
-        else blk = nt * 2 + (wn * WROWS) / 128;
-        const float* wsf = (kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
-                                   : p.w2_sf + (size_t)le * (p.H >> 7) * KB) + (size_t)blk * KB;
-        const uint32_t* dst = p.pool_dst + row0 + sm_row;
-        iSm = (sm_role == 1 ? reinterpret_cast<const uint8_t*>(wsf)
-             : sm_role == 2 ? reinterpret_cast<const uint8_t*>(dst) : reinterpret_cast<const uint8_t*>(asf)) +
-              (size_t)ikc * sm_inc;
+        iSc = static_cast<const uint8_t*>(
+            sgpr_ptr((kGemm1 ? p.pool_sf : p.l2_sf) + ((size_t)b * KB + ikc) * BM));
+        if constexpr (!kFp4) {
+            // GEMM1: the gate block nt (the up block is I/128 blocks further); GEMM2: the wave's block
+            const int blk = kGemm1 ? nt : nt * 2 + (wn * WROWS) / 128;
+            iWsc = static_cast<const uint8_t*>(sgpr_ptr((kGemm1 ? p.w1_sf + (size_t)le * ((2 * p.I) >> 7) * KB
+                                                                : p.w2_sf + (size_t)le * (p.H >> 7) * KB) +
+                                                        (size_t)blk * KB + ikc));
+        }
+        if constexpr (!kGemm1) iDst = static_cast<const uint8_t*>(sgpr_ptr(p.pool_dst + row0));
     };
-    set_issue_tile();
-    // the DMA of one K step into stage buf: straight-line code, every lane active
+    set_issue_tile(-1);
+    // the DMA of one K step into stage buf: straight-line code, every lane active (the probe: lane 0)
     auto issue_dma = [&](auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
 #pragma unroll
@@ -505,29 +626,55 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             if constexpr (kStreamW) dma16_nt(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
             else dma16(iW, b_off[i], &sB[buf][(i * NW + wave) * 1024]);
         }
-        dma4_lane(iSm, &sSmall[buf][wave * 64]);
-        if constexpr (kFp4) dma4_lane(iWs, &sWs[buf][wave * 64]);
+        if constexpr (kLaneSmall) {
+            dma4_lane(iSm, &sSmall[buf][wave * 64]);
+            if constexpr (kFp4) dma4_lane(iWsl, &sWs[buf][wave * 64]);
+        } else {
+            if (sc_lane) dma4(iSc, sm_off, &sSmall[buf][wave * 64]);
+            if constexpr (!kFp4) {
+                if (ws_lane) dma4(iWsc, sm_off, &sSmall[buf][wave * 64]);
+            }
+            if constexpr (!kGemm1) {
+                if (tg_lane) dma4(iDst, sm_off, &sSmall[buf][wave * 64]);
+            }
+            if constexpr (kFp4) dma4(iWs, ws_off, &sWs[buf][wave * 64]);
+        }
+        if constexpr (kWait != kWaitNone) {
+            if (lane == 0) dma4_coherent(iProbe, &sProbe[buf][wave]);
+        }
     };
     // advance to the next step; past the last step the last step is loaded again (constant DMA count)
-    auto issue_advance = [&]() __attribute__((always_inline)) {
+    auto issue_advance = [&](int landed) __attribute__((always_inline)) {
         if (ikb + 1 < KB) {
             ++ikb;
             if (!kRotate || ++ikc < KB) {
                 iA += BM * 128;
                 iW += 256 * WRB;
-                iSm += sm_inc;
-                if constexpr (kFp4) iWs += 1024;
+                if constexpr (kLaneSmall) {
+                    iSm += sm_inc;
+                    if constexpr (kFp4) iWsl += 1024;
+                } else {
+                    iSc += BM * 4;
+                    if constexpr (!kFp4) iWsc += 4;
+                    if constexpr (kFp4) iWs += 1024;
+                }
             } else {                                    // wrap to K block 0
                 ikc = 0;
                 iA -= (size_t)(KB - 1) * BM * 128;
                 iW -= (size_t)(KB - 1) * 256 * WRB;
-                iSm -= (size_t)(KB - 1) * sm_inc;
-                if constexpr (kFp4) iWs -= (size_t)(KB - 1) * 1024;
+                if constexpr (kLaneSmall) {
+                    iSm -= (size_t)(KB - 1) * sm_inc;
+                    if constexpr (kFp4) iWsl -= (size_t)(KB - 1) * 1024;
+                } else {
+                    iSc -= (size_t)(KB - 1) * BM * 4;
+                    if constexpr (!kFp4) iWsc -= (size_t)(KB - 1) * 4;
+                    if constexpr (kFp4) iWs -= (size_t)(KB - 1) * 1024;
+                }
             }
         } else if (ij + 1 < my_tiles) {
             ikb = 0;
             ++ij;
-            set_issue_tile();
+            set_issue_tile(landed);
         }
     };
 
@@ -615,6 +762,15 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
             constexpr int HA = WN / 2;
             static_assert(HA == 2 && HC == 32 && NWN == 4, "GEMM1 epilogue store layout");
             float h[HA][TM][4];
+            const int I = p.I;
+            // Per-lane parts of the store addresses, laundered here so that the 64-bit addresses are
+            // formed once per tile from them and wave-uniform bases, not hoisted out of the loop.
+            uint32_t ln = (uint32_t)__lane_id();
+            asm volatile("" : "+v"(ln));
+            const uint32_t lr = ln & 15u, lg = ln >> 4;
+            const uint32_t lo_go = (lr * 2u * (uint32_t)I + 4u * lg) * 4u;  // fp32 GEMM1 output (tests)
+            const uint32_t lo_l2 = lr * 32u + lg * 8u;                      // L2 pool codes
+            const uint32_t lo_sf = lr * 4u;                                 // L2 pool scales
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 float m = 0.f;
@@ -627,12 +783,20 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                         h[a][t][i] = v;
                         m = fmaxf(m, fabsf(v));
                     }
+                if (p.gemm1_out) {      // (tests) the fp32 GEMM1 output, while the accumulators live
+                    char* go = reinterpret_cast<char*>(p.gemm1_out + (row0 + wm * (BM / 2) + t * 16) * (size_t)(2 * I) +
+                                                       nt * 128 + wn * HC) + lo_go;
+#pragma unroll
+                    for (int a = 0; a < HA; ++a) {
+                        *reinterpret_cast<v4f*>(go + a * 64) = acc[a][t];
+                        *reinterpret_cast<v4f*>(go + (size_t)I * 4 + a * 64) = acc[a + HA][t];
+                    }
+                }
                 m = fmaxf(m, __shfl_xor(m, 16));
                 m = fmaxf(m, __shfl_xor(m, 32));
                 if (g == 0) sRed[wm * (BM / 2) + t * 16 + rr][wn] = m;
             }
             lds_barrier();
-            const int I = p.I;
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 const int tok = wm * (BM / 2) + t * 16 + rr;
@@ -640,7 +804,6 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
                 for (int w = 1; w < NWN; ++w) am = fmaxf(am, sRed[tok][w]);
                 const float sc = fmaxf(am, 1e-4f) / 448.0f;
-                const size_t row = row0 + tok;
                 // codes of columns 16a + 4g .. +3 of the wave's HC = 32, one dword per a
                 uint32_t q[HA];
 #pragma unroll
@@ -652,19 +815,19 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
                 // L2 pool: K block nt of GEMM2 is this n tile, stored as four 32-byte column quarters of
                 // BM rows; this wave's quarter is wn, so its 16 tokens' 32 bytes are 512 contiguous bytes
                 *reinterpret_cast<uint2*>(p.l2_x + ((size_t)b * (I >> 7) + nt) * BM * 128 + (size_t)wn * BM * 32 +
-                                          (size_t)tok * 32 + g * 8) = uint2{s16[0], s16[1]};
-                if (p.gemm1_out) {
-                    float* go = p.gemm1_out + row * (size_t)(2 * I);
-#pragma unroll
-                    for (int a = 0; a < HA; ++a) {
-                        const int col = nt * 128 + wn * HC + a * 16 + 4 * g;
-                        *reinterpret_cast<v4f*>(go + col) = acc[a][t];
-                        *reinterpret_cast<v4f*>(go + I + col) = acc[a + HA][t];
-                    }
-                }
-                if (wn == 0 && g == 0) p.l2_sf[((size_t)b * (I >> 7) + nt) * BM + tok] = sc;
+                                          (size_t)(wm * (BM / 2) + t * 16) * 32 + lo_l2) = uint2{s16[0], s16[1]};
+                if (wn == 0 && g == 0)
+                    *reinterpret_cast<float*>(reinterpret_cast<char*>(p.l2_sf + ((size_t)b * (I >> 7) + nt) * BM +
+                                                                      wm * (BM / 2) + t * 16) + lo_sf) = sc;
             }
-            lds_barrier();      // sRed is rewritten by the next tile
+            if constexpr (kPublish) {
+                // every wave's stores of the tile have completed (they sit in this XCD's L2); then one
+                // lane counts the tile in its block's word.  sRed is free again after the barrier.
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (wave == 0 && lane == 0) atomicAdd(p.sched + kSchedArrival + p.max_blocks + b, 1u);
+            } else {
+                lds_barrier();      // sRed is rewritten by the next tile
+            }
         } else {
             // The wave's output: 16-token groups t, each token 64 bf16 columns (one 128-byte line of
             // its combine row).  After the MFMA, lane (rr, g) holds columns 16a + 4g .. +3 of token rr
@@ -706,9 +869,9 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 
     // Promotion of MFMA k runs kLag MFMAs after it was issued (a ring of kRing products), so the
     // VALU never waits on the matrix core; the last kLag promotions of a step run at the start of
-    // the next one, with the previous step's factors.  The launch that also pulls the pool keeps a
-    // ring of 4 and a lag of 2: its per-tile arrival check inside the loop needs the registers.
-    constexpr int kLag = kFill ? 2 : 3, kRing = kFill ? 4 : 8;
+    // the next one, with the previous step's factors.  A ring of 4 measured as fast as one of 8 and
+    // leaves the registers to the per-tile bookkeeping.
+    constexpr int kLag = 3, kRing = 4;
     static_assert(NMF % kRing == 0 && kLag < kRing && kLag <= NMF / 2, "promotion ring");
     v4f P[kRing];
     Frags F[2];
@@ -759,7 +922,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
         for (int a = 0; a < WN; ++a)
 #pragma unroll
             for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(acc[a][t]));
-        issue_advance();
+        issue_advance((buf + 1) % kStages);
         if (++ckb == KB) {
 #pragma unroll
             for (int k = NMF - kLag; k < NMF; ++k) {
@@ -783,12 +946,12 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) F[1].sc[j][t] = 0.f;
     issue_dma(ic<0>{});
-    issue_advance();
+    issue_advance(-1);
     // the other stages of the prologue
     auto prologue = [&](auto self, auto ic_j) __attribute__((always_inline)) {
         constexpr int j = decltype(ic_j)::value;
         issue_dma(ic<j>{});
-        issue_advance();
+        issue_advance(-1);
         if constexpr (j + 1 < kStages) self(self, ic<j + 1>{});
     };
     prologue(prologue, ic<1>{});
@@ -806,15 +969,69 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     };
     for (int s = 0; s < nsteps; s += kUnroll)
         if (!steps(s, steps, ic<0>{})) break;
-    wait_all_vm();      // no LDS DMA may still be landing when the work-group ends
-    if constexpr (kFill) sched_exit(p, nblocks, tid);
+    wait_all_vm();      // no LDS DMA may still be landing when the phase ends
 }
 
-template <int BM, bool kGemm1, bool kFill = false, bool kStreamW = false, bool kFp4 = false>
+// expert offsets of the pool in LDS: the expert of a block is found there, so the pipeline never
+// waits on a global load of its own
+template <int BM, int NW, bool kFp4>
+__device__ __forceinline__ void load_offsets(const Params& p) {
+    auto& sOff = GemmLds<BM, NW, kFp4>::sOff();
+    for (int i = threadIdx.x; i <= p.El + p.nsh; i += NW * 64) sOff[i] = p.pool_off[i];
+    __syncthreads();
+}
+
+// Stream-ordered launch of one GEMM: the tiles of every pool block, spread over all work-groups.  Tiles
+// map XCD-aware: work-group i runs on XCD i mod 8 and takes a run of the tile order with the other
+// work-groups of that XCD.
+template <int BM, int NW, bool kGemm1, bool kStreamW, bool kFp4>
+__global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
+    const int nblocks = min((int)p.status[1], p.max_blocks);
+    const int G = gridDim.x;                    // a multiple of 8
+    const TilePlan plan{0, nblocks, (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3), G};
+    load_offsets<BM, NW, kFp4>(p);
+    gemm_phase<BM, NW, kGemm1, kStreamW, kFp4, kWaitNone, false, false>(p, plan, nblocks);
+}
+
+// Launch whose work-groups hand rows over by XCD (see the top of this section): [pull the pool rows
+// (kFill),] GEMM1 [, then GEMM2 (kBoth)] over the pool blocks of the work-group's XCD.
+template <int BM, int NW, bool kFill, bool kBoth, bool kStreamW, bool kFp4>
+__global__ __launch_bounds__(NW * 64, 1) void xcd_gemm_kernel(Params p) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nblocks = min((int)p.status[1], p.max_blocks);
+    const int W = gridDim.x / kXcds;            // work-groups per XCD (the host launches 8 W, W <= 32)
+    const int x = xcc_id(), slot = blockIdx.x / kXcds;
+    if (tid == 0) {
+        const uint32_t bit = 1u << slot;
+        const uint32_t old = x < kXcds ? atomicOr(p.sched + kSchedXcdSlots + x, bit) : bit;
+        if (old & bit) atomicOr(p.status, MEGA_MOE_STATUS_PLACEMENT);
+    }
+    const int xs = min(x, kXcds - 1);
+    const TilePlan plan{xs * nblocks / kXcds, (xs + 1) * nblocks / kXcds, slot, W};
+    load_offsets<BM, NW, kFp4>(p);
+    if constexpr (kFill) fill_blocks<BM>(p, plan.blo, plan.bhi, p.sched + kSchedXcdClaim + xs, lane);
+    gemm_phase<BM, NW, true, kStreamW, kFp4, kFill ? kWaitFill : kWaitNone, kBoth, true>(p, plan, nblocks);
+    if constexpr (kBoth) {
+        __syncthreads();
+        gemm_phase<BM, NW, false, kStreamW, kFp4, kWaitGemm1, false, true>(p, plan, nblocks);
+    }
+    sched_exit(p, nblocks, tid);
+}
+
+template <int BM, bool kGemm1, bool kStreamW = false, bool kFp4 = false>
 hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     int grid = (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kFill, kStreamW, kFp4>), dim3(grid), dim3(kWaves * 64),
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kStreamW, kFp4>), dim3(grid), dim3(kWaves * 64),
                        0, stream, p);
+    return hipGetLastError();
+}
+
+template <int BM, bool kFill, bool kBoth, bool kStreamW = false, bool kFp4 = false>
+hipError_t launch_xcd(const Params& p, int num_cus, hipStream_t stream) {
+    const int grid = (num_cus + 7) / 8 * 8;
+    if (grid / kXcds > 32) return hipErrorInvalidConfiguration;     // one slot word per XCD
+    hipLaunchKernelGGL((xcd_gemm_kernel<BM, kWaves, kFill, kBoth, kStreamW, kFp4>), dim3(grid),
+                       dim3(kWaves * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -827,27 +1044,45 @@ bool weights_stream(const Params& p) { return (double)p.S * p.T_max * p.K / p.E 
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
     if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
         if (p.BM == 64)
-            return weights_stream(p) ? launch<64, true, false, true, true>(p, num_cus, stream)
-                                     : launch<64, true, false, false, true>(p, num_cus, stream);
-        return launch<128, true, false, false, true>(p, num_cus, stream);
+            return weights_stream(p) ? launch<64, true, true, true>(p, num_cus, stream)
+                                     : launch<64, true, false, true>(p, num_cus, stream);
+        return launch<128, true, false, true>(p, num_cus, stream);
     }
     if (fuse_fill)
-        return p.BM == 64 ? launch<64, true, true>(p, num_cus, stream) : launch<128, true, true>(p, num_cus, stream);
+        return p.BM == 64 ? launch_xcd<64, true, false>(p, num_cus, stream)
+                          : launch_xcd<128, true, false>(p, num_cus, stream);
     if (p.BM == 64)
-        return weights_stream(p) ? launch<64, true, false, true>(p, num_cus, stream) : launch<64, true>(p, num_cus, stream);
+        return weights_stream(p) ? launch<64, true, true>(p, num_cus, stream) : launch<64, true>(p, num_cus, stream);
     return launch<128, true>(p, num_cus, stream);
 }
 
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream) {
     if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
         if (p.BM == 64)
-            return weights_stream(p) ? launch<64, false, false, true, true>(p, num_cus, stream)
-                                     : launch<64, false, false, false, true>(p, num_cus, stream);
-        return launch<128, false, false, false, true>(p, num_cus, stream);
+            return weights_stream(p) ? launch<64, false, true, true>(p, num_cus, stream)
+                                     : launch<64, false, false, true>(p, num_cus, stream);
+        return launch<128, false, false, true>(p, num_cus, stream);
     }
     if (p.BM == 64)
-        return weights_stream(p) ? launch<64, false, false, true>(p, num_cus, stream) : launch<64, false>(p, num_cus, stream);
+        return weights_stream(p) ? launch<64, false, true>(p, num_cus, stream) : launch<64, false>(p, num_cus, stream);
     return launch<128, false>(p, num_cus, stream);
+}
+
+hipError_t launch_gemms(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
+    const bool sw = p.BM == 64 && weights_stream(p);
+    if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
+        if (p.BM == 64)
+            return sw ? launch_xcd<64, false, true, true, true>(p, num_cus, stream)
+                      : launch_xcd<64, false, true, false, true>(p, num_cus, stream);
+        return launch_xcd<128, false, true, false, true>(p, num_cus, stream);
+    }
+    if (fuse_fill)
+        return p.BM == 64 ? (sw ? launch_xcd<64, true, true, true>(p, num_cus, stream)
+                                : launch_xcd<64, true, true>(p, num_cus, stream))
+                          : launch_xcd<128, true, true>(p, num_cus, stream);
+    if (p.BM == 64)
+        return sw ? launch_xcd<64, false, true, true>(p, num_cus, stream) : launch_xcd<64, false, true>(p, num_cus, stream);
+    return launch_xcd<128, false, true>(p, num_cus, stream);
 }
 
 }  // namespace mm

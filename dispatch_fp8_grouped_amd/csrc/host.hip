@@ -57,7 +57,8 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->topk < 1 || c->topk > MEGA_MOE_MAX_TOPK) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->block_m != 0 && c->block_m != 64 && c->block_m != 128) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->flags & ~(MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT | MEGA_MOE_FLAG_FILL_IN_GEMM1 |
-                     MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT | MEGA_MOE_FLAG_DEBUG_POISON)) return MEGA_MOE_ERR_UNSUPPORTED;
+                     MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT | MEGA_MOE_FLAG_DEBUG_POISON |
+                     MEGA_MOE_FLAG_ONE_GEMM_LAUNCH)) return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
     // the shared expert reads the own shard and takes combine slot K (a lane of the combine's ballot)
@@ -117,7 +118,7 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->l2_sf = take(rows * (I / 128) * 4);
     L->comb = take(((K + nsh) * S * T + 1) * H * 2);   // + one spare row: GEMM2 stores padding rows there
     L->gemm1_out = (c->flags & MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) ? take(rows * 2 * I * 4) : 0;
-    L->sched = take((mm::kSchedArrival + max_blocks) * 4);
+    L->sched = take((mm::kSchedArrival + 2 * max_blocks) * 4);
     L->total = o;
 }
 
@@ -224,9 +225,11 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
     p.cum = a.cum;
 
     int32_t rc = MEGA_MOE_OK;
-    // with FILL_IN_GEMM1 (and both stages selected) the fill runs inside GEMM1's launch
+    // with FILL_IN_GEMM1 (and both stages selected) the fill runs inside GEMM1's launch; with
+    // ONE_GEMM_LAUNCH (and both GEMMs selected) GEMM2 runs inside it too
     const bool fused_fill = fill && g1 && (c.flags & MEGA_MOE_FLAG_FILL_IN_GEMM1);
-    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill && !fused_fill, g1, g2, comb};
+    const bool one_launch = g1 && g2 && (c.flags & MEGA_MOE_FLAG_ONE_GEMM_LAUNCH);
+    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill && !fused_fill, g1, g2 && !one_launch, comb};
     const bool timing = h && h->timing;
     const int set = h ? h->next_set % kTimingSets : 0;
     if (timing && h->pending[set] && fold_times(h, set) != MEGA_MOE_OK) rc = MEGA_MOE_ERR_HIP;
@@ -256,7 +259,10 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
             switch (i) {
                 case 0: e = mm::launch_route(p, st); break;
                 case 1: e = mm::launch_fill(p, num_cus, st); break;
-                case 2: e = mm::launch_gemm1(p, fused_fill, num_cus, st); break;
+                case 2:
+                    e = one_launch ? mm::launch_gemms(p, fused_fill, num_cus, st)
+                                   : mm::launch_gemm1(p, fused_fill, num_cus, st);
+                    break;
                 case 3: e = mm::launch_gemm2(p, num_cus, st); break;
                 default: e = mm::launch_combine(p, st); break;
             }
@@ -455,7 +461,7 @@ int32_t mega_moe_forward_noalloc(const mega_moe_config* cfg, const int32_t* toke
     if (slot.err != hipSuccess || !slot.ptr) return MEGA_MOE_ERR_HIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* w = slot.ptr;
-    // what must start at zero: the status word (latched bits) and the FILL_IN_GEMM1 schedule words; every
+    // what must start at zero: the status word (latched bits) and the schedule words; every
     // other region is written by an earlier stage of the same forward before it is read
     const int sched_words = (int)((L.total - L.sched) / 4);
     hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(w + L.status), 1);

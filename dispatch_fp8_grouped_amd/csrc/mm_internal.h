@@ -12,10 +12,13 @@ constexpr int kRouteChunk = 256;       // flat (token, k) entries per routing wo
 constexpr int kBK = 128;               // GEMM K step = one scale block
 constexpr int kBN = 256;               // GEMM weight rows per tile
 constexpr uint32_t kMetaPad = 0xFFFFFFFFu;
-// Schedule words of the fill-inside-GEMM1 launch (workspace region `sched`, zero between forwards)
-constexpr int kSchedClaim = 0;         // next fill unit to claim
+// Schedule words of the launches that hand rows over inside (workspace region `sched`, zero between
+// forwards)
 constexpr int kSchedExit = 2;          // work-groups that have finished
-constexpr int kSchedArrival = 64;      // [kSchedArrival + b]: completed fill units of pool block b
+constexpr int kSchedXcdClaim = 8;      // [8 + x]: next fill unit of XCD x to claim
+constexpr int kSchedXcdSlots = 16;     // [16 + x]: bit r = the work-group in slot r of XCD x has started
+constexpr int kSchedArrival = 64;      // [64 + b]: completed fill units of pool block b, then
+                                       // [64 + max_blocks + b]: completed GEMM1 n tiles of pool block b
 
 // Everything a kernel needs, passed by value (kernel arguments).
 struct Params {
@@ -48,7 +51,7 @@ struct Params {
     float* l2_sf;         // [blocks][I/128][BM], the same block-major order
     uint16_t* comb;       // [K][S*T_max][H]
     float* gemm1_out;     // [rows][2I] or null
-    uint32_t* sched;      // kSched* words, then the per-block arrival counts
+    uint32_t* sched;      // kSched* words, then the per-block fill and GEMM1 counts
     // caller tensors
     const uint8_t* x;
     const float* x_sf;
@@ -68,6 +71,8 @@ hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream);
 // fuse_fill: GEMM1's work-groups also pull the pool rows, and each tile waits for its block's arrival
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream);
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
+// GEMM1 and GEMM2 in one launch (fuse_fill: the pool rows are pulled in it as well)
+hipError_t launch_gemms(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
 hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
                        int num_cus, hipStream_t stream);

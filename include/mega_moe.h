@@ -61,28 +61,42 @@ extern "C" {
 #define MEGA_MOE_STATUS_BAD_LAYOUT 0x4u        /* a stage found workspace metadata no earlier stage wrote
                                                   (only after mega_moe_forward_stages on hand-made data);
                                                   the affected rows were skipped */
-#define MEGA_MOE_STATUS_TIMEOUT 0x8u           /* FILL_IN_GEMM1: a GEMM1 wave waited more than about 2 s
-                                                  for pool rows to arrive (never expected: every counted
-                                                  unit is claimed by a running wave); the wait was
-                                                  abandoned and the output is undefined */
+#define MEGA_MOE_STATUS_TIMEOUT 0x8u           /* FILL_IN_GEMM1 / ONE_GEMM_LAUNCH: a GEMM wave waited more
+                                                  than about 2 s for pool rows or GEMM1 tiles of its block
+                                                  (never expected: every counted unit is held by a running
+                                                  wave); the wait was abandoned and the output is
+                                                  undefined */
+#define MEGA_MOE_STATUS_PLACEMENT 0x10u        /* FILL_IN_GEMM1 / ONE_GEMM_LAUNCH: two work-groups found
+                                                  themselves in the same (XCD, slot), so the hardware did
+                                                  not spread the launch round-robin over the eight XCDs
+                                                  (never expected on MI355X); the output is undefined */
 
 /* Config flags. */
 #define MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT 0x1u   /* also store GEMM1's fp32 output [pool_rows, 2I] (tests) */
 #define MEGA_MOE_FLAG_FILL_IN_GEMM1 0x2u       /* schedule of the pages ("Mega-MoE notes, part 2: index table
                                                   and pull", 2.6): GEMM1's work-groups pull the pool rows
-                                                  themselves, counting each block's arrival, and GEMM1 waits
-                                                  on those counts instead of a kernel boundary.  Same
-                                                  results bit for bit; slower on MI355X (each published unit
-                                                  costs a device-scope L2 writeback), so off by default */
-#define MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT 0x4u /* tests: with FILL_IN_GEMM1, every bounded wait gives up at
-                                                  once and latches MEGA_MOE_STATUS_TIMEOUT (the kernel
-                                                  still exits normally and zeroes its schedule words; the
-                                                  output is undefined) */
+                                                  themselves, counting each block's arrival, and a GEMM1
+                                                  tile waits on its block's count instead of a kernel
+                                                  boundary.  Each XCD pulls and computes its own range of
+                                                  pool blocks, so the hand-over stays in its L2.  Same
+                                                  results bit for bit */
+#define MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT 0x4u /* tests: with FILL_IN_GEMM1 or ONE_GEMM_LAUNCH, every bounded
+                                                  wait gives up at once and latches MEGA_MOE_STATUS_TIMEOUT
+                                                  (the kernel still exits normally and zeroes its schedule
+                                                  words; the output is undefined) */
 #define MEGA_MOE_FLAG_DEBUG_POISON 0x8u        /* tests: before each forward, fill the pool, its scales, the
                                                   L2 pool, its scales and the combine buffer with 0xFF bytes
                                                   (NaN as e4m3fn, fp32 and bf16), so any value read before
                                                   this forward wrote it turns the output into NaN (uses
                                                   hipMemsetAsync: not for graph capture) */
+#define MEGA_MOE_FLAG_ONE_GEMM_LAUNCH 0x10u    /* GEMM1 and GEMM2 in one persistent launch ("MoE fused
+                                                  operators", DeepGEMM part, 2: the L2 GEMM waits per m
+                                                  block for its L1 n tiles): each XCD runs the GEMM1 tiles
+                                                  of its range of pool blocks, counting each block's
+                                                  finished n tiles, then their GEMM2 tiles, each of which
+                                                  waits on its block's count.  Same results bit for bit.
+                                                  With FILL_IN_GEMM1 the launch also pulls the pool rows.
+                                                  Timed as GEMM1 (GEMM2 reads 0) */
 
 /* Weight formats (mega_moe_config.weight_format). */
 #define MEGA_MOE_WEIGHTS_FP8 0      /* e4m3fn codes, fp32 scales per 128x128 block                      */
@@ -98,7 +112,9 @@ extern "C" {
                                       /* outputs).  With GEMM1 also selected and FILL_IN_GEMM1 set it  */
                                       /* runs inside GEMM1's launch, timed as part of GEMM1             */
 #define MEGA_MOE_STAGE_GEMM1 0x4u     /* gate_up GEMM + SwiGLU + FP8 requant into the L2 pool          */
-#define MEGA_MOE_STAGE_GEMM2 0x8u     /* down GEMM, bf16, scatter to the combine buffer                */
+#define MEGA_MOE_STAGE_GEMM2 0x8u     /* down GEMM, bf16, scatter to the combine buffer.  With GEMM1  */
+                                      /* also selected and ONE_GEMM_LAUNCH set it runs inside GEMM1's  */
+                                      /* launch, timed as part of GEMM1                                */
 #define MEGA_MOE_STAGE_COMBINE 0x10u  /* top-k weighted combine into y                                 */
 #define MEGA_MOE_STAGE_ALL 0x1Fu
 #define MEGA_MOE_NUM_STAGES 5
@@ -158,9 +174,11 @@ typedef struct mega_moe_layout {
                               /* (plane K: the shared expert's rows of the own shard), then one    */
                               /* spare row that takes GEMM2's padding rows                        */
     uint64_t gemm1_out;       /* float [max_pool_blocks*BM][2I] if MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT  */
-    uint64_t sched;           /* uint32 [64 + max_pool_blocks]: FILL_IN_GEMM1 schedule: [0] next     */
-                              /*   fill unit to claim, [2] exit ticket, [64 + b]                  */
-                              /*   units of pool block b done; all zero between forwards            */
+    uint64_t sched;           /* uint32 [64 + 2*max_pool_blocks]: schedule words of FILL_IN_GEMM1 / */
+                              /*   ONE_GEMM_LAUNCH: [2] exit ticket, [8 + x] next fill unit of XCD  */
+                              /*   x, [16 + x] slots of XCD x taken, [64 + b] fill units of pool    */
+                              /*   block b done, [64 + max_pool_blocks + b] GEMM1 n tiles of block  */
+                              /*   b done; all zero between forwards                               */
     uint64_t total;           /* bytes needed                                                     */
 } mega_moe_layout;
 

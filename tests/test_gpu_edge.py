@@ -246,6 +246,13 @@ def test_stage_timing():
     t, n = mm.mega_moe_stage_times(fused.h, with_count=True)
     assert n == 1 and t[1] == 0 and all(t[i] > 0 for i in (0, 2, 3, 4))
     fused.close()
+    # GEMM2 inside GEMM1's launch is timed with GEMM1
+    one = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_ONE_GEMM_LAUNCH)
+    mm.mega_moe_set_timing(one.h, True)
+    one(inp)
+    t, n = mm.mega_moe_stage_times(one.h, with_count=True)
+    assert n == 1 and t[3] == 0 and all(t[i] > 0 for i in (0, 1, 2, 4))
+    one.close()
 
 
 @pytest.mark.parametrize("case", ["zipf_uneven", "many_shards"])
@@ -283,25 +290,37 @@ def test_route_stage_places_pool_rows(case):
 
 
 def _sched_words(moe):
-    n = 64 + moe.layout["max_pool_blocks"]
+    n = 64 + 2 * moe.layout["max_pool_blocks"]
     return moe.region("sched", torch.int32, (n,)).cpu().numpy()
 
 
-@pytest.mark.parametrize("case", ["bm64_ragged", "bm128_zipf"])
-def test_fill_inside_gemm1_matches_separate_fill(case):
-    """The FILL_IN_GEMM1 schedule (GEMM1's work-groups pull the pool and wait on arrival counts) gives
-    the same pool, L2 pool and output bits as the stream-ordered fill kernel, and leaves every schedule
-    word at zero."""
-    print(f"[case] fill inside GEMM1 vs separate fill {case}", flush=True)
+_SCHEDULES = {"fill": mm.FLAG_FILL_IN_GEMM1, "one": mm.FLAG_ONE_GEMM_LAUNCH,
+              "fill_one": mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH}
+
+
+@pytest.mark.parametrize("sched", list(_SCHEDULES))
+@pytest.mark.parametrize("case", ["bm64_ragged", "bm128_zipf", "bm128_mxfp4"])
+def test_in_launch_schedules_match_stream_order(case, sched):
+    """The schedules that hand rows over inside one launch, per XCD: FILL_IN_GEMM1 (GEMM1's work-groups
+    pull the pool and wait on per-block arrival counts), ONE_GEMM_LAUNCH (GEMM2 tiles wait on their
+    block's count of finished GEMM1 n tiles) and both together.  Each gives the same pool, L2 pool and
+    output bits as the stream-ordered kernels, reports no status bit and leaves every schedule word at
+    zero."""
+    print(f"[case] in-launch schedule {sched} vs stream order {case}", flush=True)
     if case == "bm64_ragged":
         sh = MoEShape("fz64", 5, 333, 1024, 256, 64, 16, 6, 64, local_rank=1, seed=41)
         tps = [333, 0, 101, 7, 250]
-    else:
+    elif case == "bm128_zipf":
         sh = MoEShape("fz128", 4, 700, 2048, 512, 64, 16, 8, 128, local_rank=2, routing="zipf", seed=42)
         tps = [700, 513, 1, 650]
+    else:
+        sh = MoEShape("fz4", 4, 500, 1024, 512, 32, 16, 8, 128, local_rank=1, weight_format="mxfp4", seed=43)
+        tps = [500, 211, 0, 480]
+        if _SCHEDULES[sched] & mm.FLAG_FILL_IN_GEMM1:
+            pytest.skip("the in-launch fill is built for FP8 weights only (the config check rejects it)")
     inp = make_inputs(sh, tokens_per_shard=tps)
     runs = []
-    for flags in (mm.FLAG_FILL_IN_GEMM1, 0):
+    for flags in (_SCHEDULES[sched], 0):
         run = Run(sh, inputs=inp, flags=flags, repeat=2)
         assert run.status == 0
         assert not _sched_words(run.moe).any(), "schedule words left non-zero"
@@ -321,19 +340,20 @@ def test_fill_inside_gemm1_matches_separate_fill(case):
         r.close()
 
 
-@pytest.mark.parametrize("wf", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("wf", ["fp8", "mxfp4", "fp8_one_launch"])
 def test_graph_capture_replays_match_eager(wf):
     """One forward captured in a HIP graph: three replays on changing input contents, with eager
     forwards and synchronisations between them, each bit-identical to the eager forward on the same
     inputs (the forward records no memset and leaves its workspace counters at zero)."""
     print(f"[case] graph capture and replays, {wf} weights", flush=True)
-    sh = MoEShape("graph", 4, 96, 512, 256, 32, 8, 4, 64, local_rank=1, weight_format=wf, seed=61)
+    flags = mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH if wf.endswith("one_launch") else 0
+    sh = MoEShape("graph", 4, 96, 512, 256, 32, 8, 4, 64, local_rank=1, weight_format=wf.split("_")[0], seed=61)
     tps = [96, 50, 0, 77]
     a = on_gpu(make_inputs(sh, tokens_per_shard=tps))
     b = on_gpu(make_inputs(sh, seed=62, tokens_per_shard=tps))
     for k in ("w1", "w1_sf", "w2", "w2_sf"):
         b[k] = a[k]
-    moe = mm.MegaMoE.from_shape(sh)
+    moe = mm.MegaMoE.from_shape(sh, flags=flags)
     moe(a)                                   # packs a's weights (and MXFP4 exponents) into a
     for k in ("w1_packed", "w2_packed", "w1_sf_packed", "w2_sf_packed"):
         if k in a:
@@ -372,16 +392,17 @@ def test_forced_timeout_latches_status_and_recovers():
     print("[case] forced wait timeout", flush=True)
     sh = MoEShape("tmo", 2, 80, 256, 128, 8, 4, 2, 64, seed=71)
     inp = on_gpu(make_inputs(sh))
-    forced = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_DEBUG_FORCE_TIMEOUT)
-    for _ in range(2):
-        forced(inp)
-        assert forced.status() == mm.STATUS_TIMEOUT
-        assert not _sched_words(forced).any()
-    forced.close()
-    run = Run(sh, inputs=inp, flags=mm.FLAG_FILL_IN_GEMM1)
-    assert run.status == 0
-    _whole(run, inputs_np(run))
-    run.close()
+    for flags in (mm.FLAG_FILL_IN_GEMM1, mm.FLAG_ONE_GEMM_LAUNCH, mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH):
+        forced = mm.MegaMoE.from_shape(sh, flags=flags | mm.FLAG_DEBUG_FORCE_TIMEOUT)
+        for _ in range(2):
+            forced(inp)
+            assert forced.status() == mm.STATUS_TIMEOUT
+            assert not _sched_words(forced).any()
+        forced.close()
+        run = Run(sh, inputs=inp, flags=flags)
+        assert run.status == 0
+        _whole(run, inputs_np(run))
+        run.close()
 
 
 @pytest.mark.parametrize("case", ["max_hidden", "max_intermediate", "max_topk", "max_shards"])
@@ -441,7 +462,7 @@ def test_two_handles_on_two_streams():
     mb.close()
 
 
-@pytest.mark.parametrize("case", ["bm64_shared", "bm128_fill_in_gemm1"])
+@pytest.mark.parametrize("case", ["bm64_shared", "bm128_fill_in_gemm1", "bm128_one_launch", "bm64_one_launch"])
 def test_poisoned_workspace_gives_identical_output(case):
     """With the pool, the L2 pool and the combine planes filled with NaN bytes before every forward,
     the output is bit-identical to a clean run: no stage reads a value this forward did not write.
@@ -450,9 +471,14 @@ def test_poisoned_workspace_gives_identical_output(case):
     if case == "bm64_shared":
         sh = MoEShape("poison64", 3, 140, 512, 256, 32, 8, 4, 64, local_rank=1, num_shared_experts=1, seed=95)
         tps, flags = [140, 61, 0], 0
+    elif case == "bm64_one_launch":
+        sh = MoEShape("poison64o", 3, 140, 512, 256, 32, 8, 4, 64, local_rank=1, num_shared_experts=1, seed=97)
+        tps, flags = [140, 61, 0], mm.FLAG_ONE_GEMM_LAUNCH
     else:
         sh = MoEShape("poison128", 4, 300, 1024, 512, 32, 8, 8, 128, local_rank=3, routing="zipf", seed=96)
         tps, flags = [300, 17, 299, 150], mm.FLAG_FILL_IN_GEMM1
+        if case == "bm128_one_launch":
+            flags |= mm.FLAG_ONE_GEMM_LAUNCH
     inp = make_inputs(sh, tokens_per_shard=tps)
     clean = Run(sh, inputs=inp, flags=flags)
     pois = Run(sh, inputs=inp, flags=flags | mm.FLAG_DEBUG_POISON, repeat=2)

@@ -174,6 +174,35 @@ def test_random_configs_fill_inside_gemm1(case):
     full_compare(sh, inputs=inp, flags=mm.FLAG_FILL_IN_GEMM1, name=f"{sh.name} fill-in-gemm1 tps={tps}")
 
 
+@pytest.mark.parametrize("case", range(len(_SWEEP)), ids=[sh.name for sh, _ in _SWEEP])
+def test_random_configs_one_gemm_launch(case):
+    """Every configuration with GEMM1 and GEMM2 in one launch (and, for FP8 weights, the pool pulled in
+    it too): the output bits equal the stream-ordered kernels', the status is clean and the schedule
+    words are back at zero."""
+    sh, tps = _SWEEP[case]
+    print(f"[case] one GEMM launch {sh.name} {sh.weight_format} tps={tps}", flush=True)
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    base = mm.MegaMoE.from_shape(sh)
+    want = base(inp)
+    torch.cuda.synchronize()
+    assert base.status() == 0
+    variants = [mm.FLAG_ONE_GEMM_LAUNCH]
+    if sh.weight_format == "fp8":
+        variants.append(mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_FILL_IN_GEMM1)
+    for flags in variants:
+        moe = mm.MegaMoE.from_shape(sh, flags=flags)
+        for _ in range(2):
+            got = moe(inp)
+            torch.cuda.synchronize()
+            assert moe.status() == 0
+            for i, n in enumerate(tps):
+                assert torch.equal(got[i, :n].view(torch.int16), want[i, :n].view(torch.int16)), (flags, i)
+        words = moe.region("sched", torch.int32, (64 + 2 * moe.layout["max_pool_blocks"],))
+        assert not words.any().item()
+        moe.close()
+    base.close()
+
+
 # --------------------------------------------------------------- full sizes, sampled values
 _FULL_VARIANTS = {"decode_shared": dict(num_shared_experts=1), "decode_mxfp4": dict(weight_format="mxfp4"),
                   "prefill_mxfp4": dict(weight_format="mxfp4")}
