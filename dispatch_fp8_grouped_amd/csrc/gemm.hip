@@ -66,9 +66,10 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
 // of one fragment read land in 16 different 16-byte bank slots whether the LDS serves 8 or 16 lanes of a
 // 128-bit read per cycle.
 __device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
-// 64-byte rows (MXFP4 weights, four 16-byte chunks): chunk c of row r at c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1),
-// so the 16 rows of a fragment read land in distinct 16-byte bank slots for 8- and 16-lane LDS cycles.
-__device__ __forceinline__ int swz4_chunk(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// 64-byte rows (MXFP4 weights, four 16-byte chunks): chunk c of row r at c ^ ((r >> 1) & 3).  Measured
+// with the LDS bank-conflict counter: this leaves the fragment reads conflict-free, while also flipping
+// with row bit 3 (as the 128-byte rows do) stalled 20% of the LDS-active cycles, as did the plain layout.
+__device__ __forceinline__ int swz4_chunk(int r, int c) { return c ^ ((r >> 1) & 3); }
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + (swz_chunk(r, c) << 4); }
 
 // Fragment of 16 rows x 128 K bytes for one MFMA operand: lane l takes row (l & 15) and the 32 bytes
@@ -498,7 +499,12 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     uint32_t a_off[A_INS], b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int r = (i * NW + wave) * 8 + (lane >> 3), c = swz_chunk(r, lane & 7);
+        const int r = (i * NW + wave) * 8 + (lane >> 3), p = swz_chunk(r, lane & 7);
+        // LDS position p of row r holds token chunk c.  Against MXFP4 weights a lane reads its token
+        // row's chunks g and g + 4 (the hardware's K order for that MFMA); those are stored at the
+        // positions the FP8 path reads as chunks 2g and 2g + 1, whose reads are free of bank conflicts
+        // (reading chunks g and g + 4 of the plain layout stalled 20% of the LDS-active cycles).
+        const int c = kFp4 ? ((p & 1) ? (p >> 1) + 4 : (p >> 1)) : p;
         // the L2 pool stores a K block as four 32-byte column quarters of BM rows each
         a_off[i] = kGemm1 ? r * 128 + c * 16 : (c >> 1) * (BM * 32) + r * 32 + (c & 1) * 16;
     }
@@ -689,9 +695,10 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     // alike only need to agree with each other, so the FP8 path hands group g the contiguous K
     // 32g..32g+31.  An FP4 operand holds the contiguous K 32g..32g+31 in its 16 bytes (checked on the
     // chip), so against MXFP4 weights the token fragment must follow the hardware order: chunks g and
-    // g + 4.
-    const uint8_t* xlo = &sA[0][0] + swz(xr, kFp4 ? g : 2 * g);
-    const uint8_t* xhi = &sA[0][0] + swz(xr, kFp4 ? g + 4 : 2 * g + 1);
+    // g + 4, which the token DMA stores where the FP8 path keeps chunks 2g and 2g + 1.  Both paths
+    // therefore read the same LDS positions.
+    const uint8_t* xlo = &sA[0][0] + swz(xr, 2 * g);
+    const uint8_t* xhi = &sA[0][0] + swz(xr, 2 * g + 1);
     const uint8_t* wlo = &sB[0][0] + (kFp4 ? 0 : swz(wr, 2 * g));
     const uint8_t* whi = &sB[0][0] + (kFp4 ? 0 : swz(wr, 2 * g + 1));
     // MXFP4: 16 bytes per lane and fragment, chunk g of the lane's 64-byte row
