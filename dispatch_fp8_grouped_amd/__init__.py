@@ -42,6 +42,7 @@ FLAG_FILL_IN_GEMM1 = 0x2
 FLAG_DEBUG_FORCE_TIMEOUT = 0x4
 FLAG_DEBUG_POISON = 0x8
 FLAG_ONE_GEMM_LAUNCH = 0x10
+FLAG_DEBUG_ROUTE_LAUNCHES = 0x20
 
 WEIGHTS_FP8 = 0
 WEIGHTS_MXFP4 = 1

@@ -58,7 +58,8 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->block_m != 0 && c->block_m != 64 && c->block_m != 128) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->flags & ~(MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT | MEGA_MOE_FLAG_FILL_IN_GEMM1 |
                      MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT | MEGA_MOE_FLAG_DEBUG_POISON |
-                     MEGA_MOE_FLAG_ONE_GEMM_LAUNCH)) return MEGA_MOE_ERR_UNSUPPORTED;
+                     MEGA_MOE_FLAG_ONE_GEMM_LAUNCH | MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES))
+        return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
     // the shared expert reads the own shard and takes combine slot K (a lane of the combine's ballot)

@@ -89,6 +89,9 @@ extern "C" {
                                                   (NaN as e4m3fn, fp32 and bf16), so any value read before
                                                   this forward wrote it turns the output into NaN (uses
                                                   hipMemsetAsync: not for graph capture) */
+#define MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES 0x20u /* tests: always route with the three-launch kernels, even
+                                                  where the one-work-group routing would be used (at most
+                                                  S*ceil(T_max*K/64) <= 32 groups of 64 entries) */
 #define MEGA_MOE_FLAG_ONE_GEMM_LAUNCH 0x10u    /* GEMM1 and GEMM2 in one persistent launch ("MoE fused
                                                   operators", DeepGEMM part, 2: the L2 GEMM waits per m
                                                   block for its L1 n tiles): each XCD runs the GEMM1 tiles

@@ -130,13 +130,15 @@ def test_bad_expert_id_sets_status_and_is_skipped():
     run.close()
 
 
-def test_slot_overflow_status_and_clamped_layout():
-    print("[case] slot overflow", flush=True)
+@pytest.mark.parametrize("route", ["one_group", "three_launches"])
+def test_slot_overflow_status_and_clamped_layout(route):
+    print(f"[case] slot overflow, routing {route}", flush=True)
     sh = MoEShape("dup", 1, 4, 256, 128, 2, 2, 2, 64, seed=24)
     inp = make_inputs(sh)
     inp["topk_idx"][:] = 0               # the same expert twice per token: 8 entries, 4 slots
     # poisoned workspace: a combine row the forward never wrote would read as NaN
-    run = Run(sh, inputs=inp, flags=mm.FLAG_DEBUG_POISON)
+    flags = mm.FLAG_DEBUG_POISON | (mm.FLAG_DEBUG_ROUTE_LAUNCHES if route == "three_launches" else 0)
+    run = Run(sh, inputs=inp, flags=flags)
     assert run.status & mm.STATUS_SLOT_OVERFLOW
     n = inputs_np(run)
     rt, _ = check_layout(run, n)
@@ -255,19 +257,24 @@ def test_stage_timing():
     one.close()
 
 
-@pytest.mark.parametrize("case", ["zipf_uneven", "many_shards"])
-def test_route_stage_places_pool_rows(case):
+@pytest.mark.parametrize("route", ["one_group", "three_launches"])
+@pytest.mark.parametrize("case", ["zipf_uneven", "many_shards", "zipf_small"])
+def test_route_stage_places_pool_rows(case, route):
     """The routing stage alone writes every pool row's metadata and scatter target (the round-robin
-    position of each table entry, padding rows all ones), over poisoned workspace contents."""
-    print(f"[case] route-only pool metadata {case}", flush=True)
+    position of each table entry, padding rows all ones), over poisoned workspace contents, with the
+    one-work-group routing of small inputs and with the three-launch routing."""
+    print(f"[case] route-only pool metadata {case}, routing {route}", flush=True)
     if case == "zipf_uneven":
         sh = MoEShape("rz", 6, 300, 256, 128, 64, 16, 6, 64, local_rank=2, routing="zipf", seed=31)
         tps = [300, 0, 17, 299, 151, 64]
-    else:
+    elif case == "many_shards":
         sh = MoEShape("rs", 64, 40, 256, 128, 32, 8, 4, 64, local_rank=1, seed=32)
         tps = [(7 * i) % 41 for i in range(64)]
+    else:                                   # small enough for the one-work-group routing
+        sh = MoEShape("rq", 2, 120, 256, 128, 64, 16, 8, 64, local_rank=3, routing="zipf", seed=33)
+        tps = [120, 77]
     inp = make_inputs(sh, tokens_per_shard=tps)
-    moe = mm.MegaMoE.from_shape(sh)
+    moe = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_DEBUG_ROUTE_LAUNCHES if route == "three_launches" else 0)
     cap = moe.layout["max_pool_blocks"] * moe.block_m
     moe.region("pool_meta", torch.int32, (cap, 3)).fill_(0x5A5A5A5A)
     moe.region("pool_dst", torch.int32, (cap,)).fill_(0x5A5A5A5A)

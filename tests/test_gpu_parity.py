@@ -203,6 +203,32 @@ def test_random_configs_one_gemm_launch(case):
     base.close()
 
 
+@pytest.mark.parametrize("case", range(len(_SWEEP)), ids=[sh.name for sh, _ in _SWEEP])
+def test_random_configs_routing_paths_agree(case):
+    """The one-work-group routing (used where the counts fit in LDS) and the three-launch routing write
+    the same counts, table, pool layout, row metadata and scatter targets, and give the same output
+    bits."""
+    sh, tps = _SWEEP[case]
+    print(f"[case] routing paths {sh.name} tps={tps}", flush=True)
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    runs = [Run(sh, inputs=inp, flags=f) for f in (0, mm.FLAG_DEBUG_ROUTE_LAUNCHES)]
+    a, b = (r.layout_host() for r in runs)
+    for k in a:
+        if k != "table":
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+    slots = np.arange(sh.max_tokens_per_shard)[None, None, :] < a["recv"][:, :, None]   # written slots
+    assert np.array_equal(a["table"][slots], b["table"][slots]), "table"
+    rows = a["nblocks"] * runs[0].moe.block_m
+    for name, width in (("pool_meta", 3), ("pool_dst", 1)):
+        ra, rb = (r.region(name, torch.int32, (rows * width,)).cpu().numpy() for r in runs)
+        assert np.array_equal(ra, rb), name
+    for i, n in enumerate(tps):
+        assert torch.equal(runs[0].y[i, :n].view(torch.int16), runs[1].y[i, :n].view(torch.int16))
+    for r in runs:
+        assert r.status == 0
+        r.close()
+
+
 # --------------------------------------------------------------- full sizes, sampled values
 _FULL_VARIANTS = {"decode_shared": dict(num_shared_experts=1), "decode_mxfp4": dict(weight_format="mxfp4"),
                   "prefill_mxfp4": dict(weight_format="mxfp4")}
