@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--one-launch", action="store_true",
                     help="run GEMM1 and GEMM2 in one persistent launch, each GEMM2 tile waiting on its pool "
                          "block's count of finished GEMM1 n tiles (default: two stream-ordered launches)")
+    ap.add_argument("--route-in-launch", action="store_true",
+                    help="routing, the pool pull and both GEMMs in one persistent launch, the routing stages "
+                         "separated by device-wide barriers (FP8 weights)")
     ap.add_argument("--cpu-experts", type=int, default=8)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="instead of the layer, run a plain elementwise copy of this many MiB five times "
@@ -152,10 +155,12 @@ def main():
     if args.weight_format != "fp8":
         shape = shape.replace(weight_format=args.weight_format)
     # the recorded HBM counters describe the default kernel configuration only
-    default_config = (shape == SHAPES[args.workload] and not args.fill_in_gemm1 and not args.one_launch)
+    default_config = (shape == SHAPES[args.workload] and not args.fill_in_gemm1 and not args.one_launch
+                      and not args.route_in_launch)
     torch.cuda.set_device(0)
     inp = make_inputs(shape, device="cuda")
-    flags = (mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0) | (mm.FLAG_ONE_GEMM_LAUNCH if args.one_launch else 0)
+    flags = ((mm.FLAG_FILL_IN_GEMM1 if args.fill_in_gemm1 else 0) | (mm.FLAG_ONE_GEMM_LAUNCH if args.one_launch else 0)
+             | (mm.FLAG_ROUTE_IN_LAUNCH if args.route_in_launch else 0))
     moe = mm.MegaMoE.from_shape(shape, flags=flags)
     y = torch.empty((shape.num_shards, shape.max_tokens_per_shard, shape.hidden), dtype=torch.bfloat16,
                     device="cuda")
@@ -216,6 +221,7 @@ def main():
     st = dict(zip(mm.STAGE_NAMES, stage_ms))
     fused = st["fill"] == 0.0       # the fill ran inside GEMM1's launch and is timed with it
     one = st["gemm2"] == 0.0        # GEMM2 ran inside GEMM1's launch and is timed with it
+    routed_in = st["route"] == 0.0  # so did the routing
     # the dominant kernel: GEMM1's launch (with GEMM2's flops when GEMM2 runs inside it)
     g1_flop = w["gemm1_flop"] + (w["gemm2_flop"] if one else 0.0)
     g1_tflops = g1_flop / (st["gemm1"] * 1e-3) / 1e12
@@ -247,20 +253,23 @@ def main():
         "gemm_pct_fp8_peak": 100.0 * gemm_tflops / FP8_PEAK_TFLOPS,
         "gemm_tflops": gemm_tflops,
         "roofline": {"bound": "mfma",
-                     "kernel": "gemm1 (" + ("pool fill + " if fused else "") + "gate_up + SwiGLU + requant" +
+                     "kernel": "gemm1 (" + ("routing + " if routed_in else "") + ("pool fill + " if fused else "") +
+                               "gate_up + SwiGLU + requant" +
                                (" + down GEMM + scatter, one launch" if one else "") + ")",
                      "achieved": g1_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": g1_tflops / FP8_PEAK_TFLOPS,
                      "traffic": measured_traffic(args.workload) if default_config else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic": ("6" if one else "4") + "*R*H*I flop per launch, R = routed rows"},
-        "schedule": ("fill inside gemm1" if fused else "stream-ordered fill kernel") +
+        "schedule": ("routing inside gemm1's launch, " if routed_in else "") +
+                    ("fill inside gemm1" if fused else "stream-ordered fill kernel") +
                     (", gemm2 inside gemm1's launch" if one else "") +
                     (", forward replayed from a HIP graph" if graph is not None else ""),
         "stages_ms": st,
         "ms_per_step_with_stage_events": ms_staged,
         "stages": {
-            "route": {"GB/s": gbs(w["route_bytes"], st["route"])},
+            "route": ({"schedule": "inside the gemm1 launch (device-wide barriers); timed with gemm1"} if routed_in
+                      else {"GB/s": gbs(w["route_bytes"], st["route"])}),
             "fill": fill_stage,
             "gemm1": {"TFLOP/s": g1_tflops, "frac": g1_tflops / FP8_PEAK_TFLOPS},
             "gemm2": ({"schedule": "inside the gemm1 launch (per-block GEMM1 counts); timed with gemm1"} if one

@@ -43,6 +43,7 @@ FLAG_DEBUG_FORCE_TIMEOUT = 0x4
 FLAG_DEBUG_POISON = 0x8
 FLAG_ONE_GEMM_LAUNCH = 0x10
 FLAG_DEBUG_ROUTE_LAUNCHES = 0x20
+FLAG_ROUTE_IN_LAUNCH = 0x40
 
 WEIGHTS_FP8 = 0
 WEIGHTS_MXFP4 = 1

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "mm_internal.h"
+#include "route_impl.h"
 
 namespace mm {
 namespace {
@@ -306,18 +307,21 @@ __device__ __forceinline__ void fill_blocks(const Params& p, int blo, int bhi, u
 // kSpinTicks latches TIMEOUT and gives up: never expected, it keeps a broken schedule from hanging the
 // GPU.  MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT makes every wait give up as soon as the clock moves, so tests
 // reach that path from the host.
-__device__ __forceinline__ void spin_until(const Params& p, const uint32_t* word, uint32_t target, int lane) {
-    const bool force = p.flags & MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT;
-    if (!force && sched_peek(word) >= target) return;
+// Returns whether the target was reached.  kForceable: MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT applies.
+template <bool kForceable = true>
+__device__ __forceinline__ bool spin_until(const Params& p, const uint32_t* word, uint32_t target, int lane) {
+    const bool force = kForceable && (p.flags & MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT);
+    if (!force && sched_peek(word) >= target) return true;
     const long long limit = force ? 0 : kSpinTicks;
     const long long t0 = wall_clock64();
     while (force || sched_peek(word) < target) {
         if (wall_clock64() - t0 > limit) {
             if (lane == 0) atomicOr(p.status, MEGA_MOE_STATUS_TIMEOUT);
-            return;
+            return false;
         }
         __builtin_amdgcn_s_sleep(32);
     }
+    return true;
 }
 
 // Every work-group takes an exit ticket after its last access to the schedule words (its atomics have
@@ -1000,11 +1004,69 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     gemm_phase<BM, NW, kGemm1, kStreamW, kFp4, kWaitNone, false, false>(p, plan, nblocks);
 }
 
-// Launch whose work-groups hand rows over by XCD (see the top of this section): [pull the pool rows
-// (kFill),] GEMM1 [, then GEMM2 (kBoth)] over the pool blocks of the work-group's XCD.
-template <int BM, int NW, bool kFill, bool kBoth, bool kStreamW, bool kFp4>
+// Device-wide barrier: every work-group's writes are released to memory (an L2 writeback) before it
+// counts itself in *ctr, and acquired (L1 and L2 invalidated) after the count reaches the grid size.
+// Needs every work-group resident at once.  The wait is bounded: past it TIMEOUT is latched and false
+// returned, and the work-group then skips the rest of the launch (what follows would read routing
+// results that are not complete).  The debug flag that forces waits to give up does not apply here.
+__device__ __forceinline__ bool grid_barrier(const Params& p, uint32_t* ctr, int tid) {
+    __shared__ int sOk;
+    __syncthreads();
+    if (tid < 64) {
+        if (tid == 0) {
+            __threadfence();
+            atomicAdd(ctr, 1u);
+        }
+        const bool ok = spin_until<false>(p, ctr, gridDim.x, tid);
+        __threadfence();
+        if (tid == 0) sOk = ok;
+    }
+    __syncthreads();
+    return sOk;
+}
+
+// Routing inside the launch, before the pull ("MoE fused operators", DeepGEMM part, 2: the expert waves
+// start after the dispatch metadata, with a grid-wide sync between; "DeepGEMM Mega MoE symmetric memory
+// deep analysis", 6: grid_sync).  The three routing stages run over all work-groups with the same code
+// as the routing kernels (route_impl.h), each ended by a device-wide barrier; their scratch is the LDS
+// of the weight stages, which the GEMM has not used yet.
+template <int BM, int NW, bool kFp4>
+__device__ __forceinline__ bool route_in_launch(const Params& p, int tid) {
+    using Lds = GemmLds<BM, NW, kFp4>;
+    int* lds = reinterpret_cast<int*>(&Lds::sB()[0][0]);
+    constexpr int kLdsInts = (int)(sizeof(Lds::sB()) / sizeof(int));
+    const int G = gridDim.x, wg = blockIdx.x, nthreads = NW * 64;
+    const int nchunk = p.chunks * p.S;
+    for (int q = wg; q < nchunk; q += G) route_count_chunk(p, q % p.chunks, q / p.chunks, lds, tid, nthreads);
+    if (!grid_barrier(p, p.sched + kSchedGridBar + 0, tid)) return false;
+    for (int s = wg; s < p.S; s += G) route_scan_shard(p, s, tid, nthreads);
+    if (!grid_barrier(p, p.sched + kSchedGridBar + 1, tid)) return false;
+    // the table: one wave per (chunk, shard), each with its own share of the LDS
+    const int wave = tid >> 6, lane = tid & 63;
+    constexpr int kWaveInts = kLdsInts / NW;
+    const int run_ints = p.El <= 64 ? 1 : p.El, off_ints = MEGA_MOE_MAX_LOCAL_EXPERTS + 2;
+    int* offs = lds + wave * kWaveInts;
+    int* run = offs + off_ints;
+    int* stage = run + run_ints;
+    const int stage_ints = kWaveInts - off_ints - run_ints;
+    for (int q = wg * NW + wave; q < nchunk; q += G * NW) {
+        if (p.El <= 64) route_table_chunk<true>(p, q % p.chunks, q / p.chunks, lane, run, stage, offs, stage_ints);
+        else route_table_chunk<false>(p, q % p.chunks, q / p.chunks, lane, run, stage, offs, stage_ints);
+    }
+    return grid_barrier(p, p.sched + kSchedGridBar + 2, tid);
+}
+
+// Launch whose work-groups hand rows over by XCD (see the top of this section): [route (kRoute),] [pull
+// the pool rows (kFill),] GEMM1 [, then GEMM2 (kBoth)] over the pool blocks of the work-group's XCD.
+template <int BM, int NW, bool kFill, bool kBoth, bool kStreamW, bool kFp4, bool kRoute = false>
 __global__ __launch_bounds__(NW * 64, 1) void xcd_gemm_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63;
+    if constexpr (kRoute) {
+        if (!route_in_launch<BM, NW, kFp4>(p, tid)) {
+            sched_exit(p, p.max_blocks, tid);      // the block count is not known: clean every block's words
+            return;
+        }
+    }
     const int nblocks = min((int)p.status[1], p.max_blocks);
     const int W = gridDim.x / kXcds;            // work-groups per XCD (the host launches 8 W, W <= 32)
     const int x = xcc_id(), slot = blockIdx.x / kXcds;
@@ -1073,6 +1135,20 @@ hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream) {
     if (p.BM == 64)
         return weights_stream(p) ? launch<64, false, true>(p, num_cus, stream) : launch<64, false>(p, num_cus, stream);
     return launch<128, false>(p, num_cus, stream);
+}
+
+hipError_t launch_route_fill_gemms(const Params& p, int num_cus, hipStream_t stream) {
+    // the routing's device-wide barriers need every work-group resident: one per CU, grid = CU count
+    if (num_cus % kXcds || num_cus / kXcds > 32 || p.wfmt != MEGA_MOE_WEIGHTS_FP8) return hipErrorInvalidConfiguration;
+    const bool sw = p.BM == 64 && weights_stream(p);
+    const dim3 grid(num_cus), block(kWaves * 64);
+    if (p.BM == 128)
+        hipLaunchKernelGGL((xcd_gemm_kernel<128, kWaves, true, true, false, false, true>), grid, block, 0, stream, p);
+    else if (sw)
+        hipLaunchKernelGGL((xcd_gemm_kernel<64, kWaves, true, true, true, false, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((xcd_gemm_kernel<64, kWaves, true, true, false, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemms(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {

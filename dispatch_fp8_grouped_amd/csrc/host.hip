@@ -58,7 +58,8 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->block_m != 0 && c->block_m != 64 && c->block_m != 128) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->flags & ~(MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT | MEGA_MOE_FLAG_FILL_IN_GEMM1 |
                      MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT | MEGA_MOE_FLAG_DEBUG_POISON |
-                     MEGA_MOE_FLAG_ONE_GEMM_LAUNCH | MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES))
+                     MEGA_MOE_FLAG_ONE_GEMM_LAUNCH | MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES |
+                     MEGA_MOE_FLAG_ROUTE_IN_LAUNCH))
         return MEGA_MOE_ERR_UNSUPPORTED;
     // table entries are int32 t*K+k
     if ((int64_t)c->max_tokens_per_shard * c->topk >= (int64_t)1 << 31) return MEGA_MOE_ERR_UNSUPPORTED;
@@ -67,8 +68,9 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->num_shared_experts && (c->local_rank >= c->num_shards || c->topk >= 64)) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->weight_format != MEGA_MOE_WEIGHTS_FP8 && c->weight_format != MEGA_MOE_WEIGHTS_MXFP4)
         return MEGA_MOE_ERR_UNSUPPORTED;
-    // the arrival-counted fill is built for FP8 weights only
-    if (c->weight_format == MEGA_MOE_WEIGHTS_MXFP4 && (c->flags & MEGA_MOE_FLAG_FILL_IN_GEMM1))
+    // the arrival-counted fill (and the launch that also routes) is built for FP8 weights only
+    if (c->weight_format == MEGA_MOE_WEIGHTS_MXFP4 &&
+        (c->flags & (MEGA_MOE_FLAG_FILL_IN_GEMM1 | MEGA_MOE_FLAG_ROUTE_IN_LAUNCH)))
         return MEGA_MOE_ERR_UNSUPPORTED;
     // pool rows and combine rows (K*S*T_max) are int32 / uint32 indices in the kernels
     if ((int64_t)c->num_shards * c->max_tokens_per_shard * (c->topk + 1) + (int64_t)c->num_local_experts * 128 +
@@ -230,7 +232,10 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
     // ONE_GEMM_LAUNCH (and both GEMMs selected) GEMM2 runs inside it too
     const bool fused_fill = fill && g1 && (c.flags & MEGA_MOE_FLAG_FILL_IN_GEMM1);
     const bool one_launch = g1 && g2 && (c.flags & MEGA_MOE_FLAG_ONE_GEMM_LAUNCH);
-    const bool on[MEGA_MOE_NUM_STAGES] = {route, fill && !fused_fill, g1, g2 && !one_launch, comb};
+    // with ROUTE_IN_LAUNCH (and routing, fill and both GEMMs selected) all four run in GEMM1's launch
+    const bool all_in_one = route && fill && g1 && g2 && (c.flags & MEGA_MOE_FLAG_ROUTE_IN_LAUNCH);
+    const bool on[MEGA_MOE_NUM_STAGES] = {route && !all_in_one, fill && !fused_fill && !all_in_one, g1,
+                                          g2 && !one_launch && !all_in_one, comb};
     const bool timing = h && h->timing;
     const int set = h ? h->next_set % kTimingSets : 0;
     if (timing && h->pending[set] && fold_times(h, set) != MEGA_MOE_OK) rc = MEGA_MOE_ERR_HIP;
@@ -261,8 +266,9 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
                 case 0: e = mm::launch_route(p, st); break;
                 case 1: e = mm::launch_fill(p, num_cus, st); break;
                 case 2:
-                    e = one_launch ? mm::launch_gemms(p, fused_fill, num_cus, st)
-                                   : mm::launch_gemm1(p, fused_fill, num_cus, st);
+                    e = all_in_one   ? mm::launch_route_fill_gemms(p, num_cus, st)
+                        : one_launch ? mm::launch_gemms(p, fused_fill, num_cus, st)
+                                     : mm::launch_gemm1(p, fused_fill, num_cus, st);
                     break;
                 case 3: e = mm::launch_gemm2(p, num_cus, st); break;
                 default: e = mm::launch_combine(p, st); break;

@@ -17,6 +17,7 @@ constexpr uint32_t kMetaPad = 0xFFFFFFFFu;
 constexpr int kSchedExit = 2;          // work-groups that have finished
 constexpr int kSchedXcdClaim = 8;      // [8 + x]: next fill unit of XCD x to claim
 constexpr int kSchedXcdSlots = 16;     // [16 + x]: bit r = the work-group in slot r of XCD x has started
+constexpr int kSchedGridBar = 40;      // [40 + i]: work-groups past device-wide barrier i of the routing
 constexpr int kSchedArrival = 64;      // [64 + b]: completed fill units of pool block b, then
                                        // [64 + max_blocks + b]: completed GEMM1 n tiles of pool block b
 
@@ -73,6 +74,8 @@ hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream);
 // GEMM1 and GEMM2 in one launch (fuse_fill: the pool rows are pulled in it as well)
 hipError_t launch_gemms(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream);
+// Routing, the pull and both GEMMs in one launch (FP8 weights; needs every work-group resident at once)
+hipError_t launch_route_fill_gemms(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
 hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
                        int num_cus, hipStream_t stream);

@@ -92,6 +92,14 @@ extern "C" {
 #define MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES 0x20u /* tests: always route with the three-launch kernels, even
                                                   where the one-work-group routing would be used (at most
                                                   S*ceil(T_max*K/64) <= 32 groups of 64 entries) */
+#define MEGA_MOE_FLAG_ROUTE_IN_LAUNCH 0x40u    /* routing, the pull and both GEMMs in one persistent launch
+                                                  (FP8 weights; all five stages selected): the routing
+                                                  stages run over all work-groups, each ended by a
+                                                  device-wide barrier ("DeepGEMM Mega MoE symmetric memory
+                                                  deep analysis", 6: grid_sync), then the launch goes on as
+                                                  with FILL_IN_GEMM1 | ONE_GEMM_LAUNCH.  Needs the whole
+                                                  GPU (one work-group per CU, all resident); the waits are
+                                                  bounded.  Same results bit for bit.  Timed as GEMM1 */
 #define MEGA_MOE_FLAG_ONE_GEMM_LAUNCH 0x10u    /* GEMM1 and GEMM2 in one persistent launch ("MoE fused
                                                   operators", DeepGEMM part, 2: the L2 GEMM waits per m
                                                   block for its L1 n tiles): each XCD runs the GEMM1 tiles

@@ -165,7 +165,8 @@ def test_weight_format_config():
                cfg_of("decode", flags=mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_FILL_IN_GEMM1)):
         assert lib.mega_moe_workspace_bytes(ctypes.byref(ok), ctypes.byref(out)) == mm.OK
     for c in (cfg_of("decode", weight_format=2), cfg_of("decode", weight_format=-1),
-              cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_FILL_IN_GEMM1)):
+              cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_FILL_IN_GEMM1),
+              cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_ROUTE_IN_LAUNCH)):
         assert lib.mega_moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == mm.ERR_UNSUPPORTED
 
 

@@ -255,6 +255,13 @@ def test_stage_timing():
     t, n = mm.mega_moe_stage_times(one.h, with_count=True)
     assert n == 1 and t[3] == 0 and all(t[i] > 0 for i in (0, 1, 2, 4))
     one.close()
+    # routing, the pull and both GEMMs in one launch: all timed with GEMM1
+    alls = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_ROUTE_IN_LAUNCH)
+    mm.mega_moe_set_timing(alls.h, True)
+    alls(inp)
+    t, n = mm.mega_moe_stage_times(alls.h, with_count=True)
+    assert n == 1 and t[0] == t[1] == t[3] == 0 and t[2] > 0 and t[4] > 0
+    alls.close()
 
 
 @pytest.mark.parametrize("route", ["one_group", "three_launches"])
@@ -302,7 +309,7 @@ def _sched_words(moe):
 
 
 _SCHEDULES = {"fill": mm.FLAG_FILL_IN_GEMM1, "one": mm.FLAG_ONE_GEMM_LAUNCH,
-              "fill_one": mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH}
+              "fill_one": mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH, "route_all": mm.FLAG_ROUTE_IN_LAUNCH}
 
 
 @pytest.mark.parametrize("sched", list(_SCHEDULES))
@@ -310,9 +317,9 @@ _SCHEDULES = {"fill": mm.FLAG_FILL_IN_GEMM1, "one": mm.FLAG_ONE_GEMM_LAUNCH,
 def test_in_launch_schedules_match_stream_order(case, sched):
     """The schedules that hand rows over inside one launch, per XCD: FILL_IN_GEMM1 (GEMM1's work-groups
     pull the pool and wait on per-block arrival counts), ONE_GEMM_LAUNCH (GEMM2 tiles wait on their
-    block's count of finished GEMM1 n tiles) and both together.  Each gives the same pool, L2 pool and
-    output bits as the stream-ordered kernels, reports no status bit and leaves every schedule word at
-    zero."""
+    block's count of finished GEMM1 n tiles), both together, and routing in the same launch behind
+    device-wide barriers.  Each gives the same pool, L2 pool and output bits as the stream-ordered
+    kernels, reports no status bit and leaves every schedule word at zero."""
     print(f"[case] in-launch schedule {sched} vs stream order {case}", flush=True)
     if case == "bm64_ragged":
         sh = MoEShape("fz64", 5, 333, 1024, 256, 64, 16, 6, 64, local_rank=1, seed=41)
@@ -323,7 +330,7 @@ def test_in_launch_schedules_match_stream_order(case, sched):
     else:
         sh = MoEShape("fz4", 4, 500, 1024, 512, 32, 16, 8, 128, local_rank=1, weight_format="mxfp4", seed=43)
         tps = [500, 211, 0, 480]
-        if _SCHEDULES[sched] & mm.FLAG_FILL_IN_GEMM1:
+        if _SCHEDULES[sched] & (mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ROUTE_IN_LAUNCH):
             pytest.skip("the in-launch fill is built for FP8 weights only (the config check rejects it)")
     inp = make_inputs(sh, tokens_per_shard=tps)
     runs = []
@@ -399,7 +406,8 @@ def test_forced_timeout_latches_status_and_recovers():
     print("[case] forced wait timeout", flush=True)
     sh = MoEShape("tmo", 2, 80, 256, 128, 8, 4, 2, 64, seed=71)
     inp = on_gpu(make_inputs(sh))
-    for flags in (mm.FLAG_FILL_IN_GEMM1, mm.FLAG_ONE_GEMM_LAUNCH, mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH):
+    for flags in (mm.FLAG_FILL_IN_GEMM1, mm.FLAG_ONE_GEMM_LAUNCH, mm.FLAG_FILL_IN_GEMM1 | mm.FLAG_ONE_GEMM_LAUNCH,
+                  mm.FLAG_ROUTE_IN_LAUNCH):
         forced = mm.MegaMoE.from_shape(sh, flags=flags | mm.FLAG_DEBUG_FORCE_TIMEOUT)
         for _ in range(2):
             forced(inp)
@@ -469,7 +477,8 @@ def test_two_handles_on_two_streams():
     mb.close()
 
 
-@pytest.mark.parametrize("case", ["bm64_shared", "bm128_fill_in_gemm1", "bm128_one_launch", "bm64_one_launch"])
+@pytest.mark.parametrize("case", ["bm64_shared", "bm128_fill_in_gemm1", "bm128_one_launch", "bm64_one_launch",
+                                  "bm128_route_in_launch"])
 def test_poisoned_workspace_gives_identical_output(case):
     """With the pool, the L2 pool and the combine planes filled with NaN bytes before every forward,
     the output is bit-identical to a clean run: no stage reads a value this forward did not write.
@@ -486,6 +495,8 @@ def test_poisoned_workspace_gives_identical_output(case):
         tps, flags = [300, 17, 299, 150], mm.FLAG_FILL_IN_GEMM1
         if case == "bm128_one_launch":
             flags |= mm.FLAG_ONE_GEMM_LAUNCH
+        elif case == "bm128_route_in_launch":
+            flags = mm.FLAG_ROUTE_IN_LAUNCH
     inp = make_inputs(sh, tokens_per_shard=tps)
     clean = Run(sh, inputs=inp, flags=flags)
     pois = Run(sh, inputs=inp, flags=flags | mm.FLAG_DEBUG_POISON, repeat=2)

@@ -177,8 +177,8 @@ def test_random_configs_fill_inside_gemm1(case):
 @pytest.mark.parametrize("case", range(len(_SWEEP)), ids=[sh.name for sh, _ in _SWEEP])
 def test_random_configs_one_gemm_launch(case):
     """Every configuration with GEMM1 and GEMM2 in one launch (and, for FP8 weights, the pool pulled in
-    it too): the output bits equal the stream-ordered kernels', the status is clean and the schedule
-    words are back at zero."""
+    it too, and routing as well): the output bits equal the stream-ordered kernels', the status is
+    clean and the schedule words are back at zero."""
     sh, tps = _SWEEP[case]
     print(f"[case] one GEMM launch {sh.name} {sh.weight_format} tps={tps}", flush=True)
     inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
@@ -188,7 +188,7 @@ def test_random_configs_one_gemm_launch(case):
     assert base.status() == 0
     variants = [mm.FLAG_ONE_GEMM_LAUNCH]
     if sh.weight_format == "fp8":
-        variants.append(mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_FILL_IN_GEMM1)
+        variants += [mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_FILL_IN_GEMM1, mm.FLAG_ROUTE_IN_LAUNCH]
     for flags in variants:
         moe = mm.MegaMoE.from_shape(sh, flags=flags)
         for _ in range(2):
