@@ -453,7 +453,11 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     constexpr int kInFlight = (kStages - 2) * DMA_PER_STEP;   // at mid-step: the steps after the next one
     static_assert((kStages - 1) * DMA_PER_STEP + kEpiStores < 64, "vmcnt immediate");
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    // The thread index is laundered, so the per-lane values of the phase are formed here: a launch that
+    // runs phases in a loop (expert waves) would otherwise keep them live across every phase.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = (wave / NWN) & 1, wn = wave % NWN;
     const int rr = lane & 15, g = lane >> 4;
@@ -1079,10 +1083,52 @@ __global__ __launch_bounds__(NW * 64, 1) void xcd_gemm_kernel(Params p) {
     const TilePlan plan{xs * nblocks / kXcds, (xs + 1) * nblocks / kXcds, slot, W};
     load_offsets<BM, NW, kFp4>(p);
     if constexpr (kFill) fill_blocks<BM>(p, plan.blo, plan.bhi, p.sched + kSchedXcdClaim + xs, lane);
-    gemm_phase<BM, NW, true, kStreamW, kFp4, kFill ? kWaitFill : kWaitNone, kBoth, true>(p, plan, nblocks);
     if constexpr (kBoth) {
+        // Expert waves ("MoE fused operators", DeepGEMM part, 2 and 5: a wave of experts runs all its L1
+        // tiles, then all its L2 tiles, and the wave is sized so its L1 tiles fill the SMs).  Here a wave
+        // is a run of whole experts of the XCD's block range whose GEMM1 tiles number at least
+        // p.wave_tiles (the host picks the XCD's work-group count, so every work-group has a GEMM1 tile
+        // in each wave); 0 makes the whole range one wave.  The boundaries are laid out in LDS first (at
+        // most kMaxWaves waves), so the loop keeps only the wave index live across the phases.
+        constexpr int kMaxWaves = 64;
+        __shared__ int sWave[kMaxWaves + 1];
+        __shared__ int sNumWaves;
+        if (tid == 0) {
+            const int NT1 = p.I >> 7, range = plan.bhi - plan.blo;
+            int target = p.wave_tiles > 0 ? p.wave_tiles : range * NT1;
+            target = max(target, (range * NT1 + kMaxWaves - 1) / kMaxWaves);
+            const auto& sOff = GemmLds<BM, NW, kFp4>::sOff();
+            const int nseg = p.El + p.nsh;
+            int n = 0, wb = plan.blo, i = 1;
+            sWave[0] = wb;
+            while (wb < plan.bhi) {
+                int we = wb;
+                while (we < plan.bhi && (we - wb) * NT1 < target) {
+                    while (i <= nseg && sOff[i] <= we) ++i;        // the next expert boundary above we
+                    we = i <= nseg ? min(sOff[i], plan.bhi) : plan.bhi;
+                }
+                sWave[++n] = we;
+                wb = we;
+            }
+            sNumWaves = n;
+        }
         __syncthreads();
-        gemm_phase<BM, NW, false, kStreamW, kFp4, kWaitGemm1, false, true>(p, plan, nblocks);
+        const int nwaves = __builtin_amdgcn_readfirstlane(sNumWaves);
+        for (int w = 0; w < nwaves; ++w) {
+            const TilePlan wave{__builtin_amdgcn_readfirstlane(sWave[w]), __builtin_amdgcn_readfirstlane(sWave[w + 1]),
+                                slot, W};
+            // The parameters are read again from the kernel-argument segment in every wave (the laundered
+            // segment address keeps the loads inside the loop), so they are not held across the phases.
+            auto pk = (const __attribute__((address_space(4))) Params*)__builtin_amdgcn_kernarg_segment_ptr();
+            asm volatile("" : "+s"(pk));
+            const Params q = *(const Params*)pk;
+            gemm_phase<BM, NW, true, kStreamW, kFp4, kFill ? kWaitFill : kWaitNone, true, true>(q, wave, nblocks);
+            __syncthreads();
+            gemm_phase<BM, NW, false, kStreamW, kFp4, kWaitGemm1, false, true>(q, wave, nblocks);
+            __syncthreads();
+        }
+    } else {
+        gemm_phase<BM, NW, true, kStreamW, kFp4, kFill ? kWaitFill : kWaitNone, false, true>(p, plan, nblocks);
     }
     sched_exit(p, nblocks, tid);
 }

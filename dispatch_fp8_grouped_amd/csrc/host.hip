@@ -190,6 +190,8 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
     p.BM = L.block_m;
     p.chunks = L.route_chunks;
     p.max_blocks = L.max_pool_blocks;
+    // one-launch GEMMs: an expert wave holds at least one GEMM1 tile per work-group of an XCD
+    p.wave_tiles = ((num_cus + 7) / 8 * 8) / 8;
     p.flags = c.flags;
     for (int s = 0; s < c.num_shards; ++s) {
         const int32_t t = a.tps[s];

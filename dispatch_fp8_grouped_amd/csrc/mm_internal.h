@@ -30,6 +30,7 @@ struct Params {
     int wfmt;             // MEGA_MOE_WEIGHTS_FP8 or MEGA_MOE_WEIGHTS_MXFP4
     int chunks;           // routing chunks per shard
     int max_blocks;       // pool capacity in BM blocks
+    int wave_tiles;       // one-launch GEMMs: GEMM1 tiles an expert wave holds at least (0: one wave)
     uint32_t flags;
     int tps[MEGA_MOE_MAX_SHARDS];
     // workspace

@@ -313,7 +313,7 @@ _SCHEDULES = {"fill": mm.FLAG_FILL_IN_GEMM1, "one": mm.FLAG_ONE_GEMM_LAUNCH,
 
 
 @pytest.mark.parametrize("sched", list(_SCHEDULES))
-@pytest.mark.parametrize("case", ["bm64_ragged", "bm128_zipf", "bm128_mxfp4"])
+@pytest.mark.parametrize("case", ["bm64_ragged", "bm128_zipf", "bm128_mxfp4", "bm128_waves"])
 def test_in_launch_schedules_match_stream_order(case, sched):
     """The schedules that hand rows over inside one launch, per XCD: FILL_IN_GEMM1 (GEMM1's work-groups
     pull the pool and wait on per-block arrival counts), ONE_GEMM_LAUNCH (GEMM2 tiles wait on their
@@ -327,6 +327,11 @@ def test_in_launch_schedules_match_stream_order(case, sched):
     elif case == "bm128_zipf":
         sh = MoEShape("fz128", 4, 700, 2048, 512, 64, 16, 8, 128, local_rank=2, routing="zipf", seed=42)
         tps = [700, 513, 1, 650]
+    elif case == "bm128_waves":
+        # 64 local experts of about two 128-row blocks each and 8 GEMM1 n tiles per block: every XCD's
+        # block range splits into several expert waves when GEMM2 shares the launch.
+        sh = MoEShape("fzw", 4, 1024, 512, 1024, 128, 64, 8, 128, local_rank=1, seed=44)
+        tps = [1024, 1000, 777, 1024]
     else:
         sh = MoEShape("fz4", 4, 500, 1024, 512, 32, 16, 8, 128, local_rank=1, weight_format="mxfp4", seed=43)
         tps = [500, 211, 0, 480]
