@@ -819,11 +819,12 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
 #pragma unroll
                 for (int w = 1; w < NWN; ++w) am = fmaxf(am, sRed[tok][w]);
                 const float sc = fmaxf(am, 1e-4f) / 448.0f;
+                const float isc = 1.0f / sc;        // codes: h times the fp32 reciprocal of the scale
                 // codes of columns 16a + 4g .. +3 of the wave's HC = 32, one dword per a
                 uint32_t q[HA];
 #pragma unroll
                 for (int a = 0; a < HA; ++a)
-                    q[a] = cvt_fp8x4(h[a][t][0] / sc, h[a][t][1] / sc, h[a][t][2] / sc, h[a][t][3] / sc);
+                    q[a] = cvt_fp8x4(h[a][t][0] * isc, h[a][t][1] * isc, h[a][t][2] * isc, h[a][t][3] * isc);
                 // (register a, lane row g) -> lane row g holds bytes 8g .. 8g+7 of the token's 32
                 const auto s32 = __builtin_amdgcn_permlane32_swap(q[0], q[1], false, false);
                 const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);

@@ -237,8 +237,9 @@ def requant_rows(h: np.ndarray, gran: int = 128):
 
     The first layer's epilogue writes FP8 activations plus scale factors for the second
     layer ("Mega-MoE kernel code walkthrough", section 6 and 8.2).  The scale rule is this
-    build's reading (the pages give none): s = max(amax, 1e-4) / 448, q = e4m3fn(h / s)
-    with ties to even and saturation.  The decision is taken in fp32, as the kernel takes it.
+    build's reading (the pages give none): s = max(amax, 1e-4) / 448, q = e4m3fn(h * (1 / s))
+    with ties to even and saturation, where 1 / s is the fp32 reciprocal and the product one fp32
+    multiply.  The decision is taken in fp32, as the kernel takes it.
     Returns (codes uint8 [M, C], scales float32 [M, C/gran]).
     """
     h32 = np.asarray(h, dtype=np.float64).astype(np.float32)
@@ -247,7 +248,8 @@ def requant_rows(h: np.ndarray, gran: int = 128):
     amax = np.abs(hb).max(axis=2)
     s = np.maximum(amax, np.float32(1e-4)).astype(np.float32) / np.float32(E4M3_MAX)
     s = s.astype(np.float32)
-    v = (hb / s[:, :, None]).astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    v = (hb * inv[:, :, None]).astype(np.float32)
     codes = e4m3fn_encode(v).reshape(M, C)
     return codes, s
 

@@ -258,6 +258,21 @@ def test_requant_closed_forms():
     assert rel.max() < 2.0 ** -4 * 1.01
 
 
+def test_requant_uses_the_fp32_reciprocal_of_the_scale():
+    """The code is decided on h * fp32(1/s), not on h / s.  For this block amax and value the two fp32
+    results are 400.0 exactly (a tie between the e4m3 codes for 384 and 416, so to even: 384) and
+    400.00003 (416); the value was found by search over random h."""
+    h = np.zeros((1, 128), dtype=np.float32)
+    h[0, 0] = np.float32(3.5609652996063232)      # the block's amax
+    h[0, 1] = np.float32(3.1794333457946777)
+    q, s = oracle.requant_rows(h)
+    assert s[0, 0] == np.float32(np.float32(3.5609652996063232) / np.float32(448))
+    assert oracle.e4m3fn_decode(q[0, 1:2])[0] == 384.0
+    # division would have rounded up
+    assert (h[0, 1] / s[0, 0]).astype(np.float32) > np.float32(400.0)
+    assert oracle.e4m3fn_decode(oracle.e4m3fn_encode(np.float32(h[0, 1] / s[0, 0])[None]))[0] == 416.0
+
+
 def test_gemm1_exact_on_integer_codes():
     """Integer codes with power-of-two scales: G equals an int64 matmul times the scales."""
     sh = MoEShape("t", 1, 32, 256, 128, 2, 2, 1, 64)
