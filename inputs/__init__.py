@@ -49,7 +49,7 @@ class MoEShape:
     local_rank: int = 0
     routing: str = "uniform"   # "uniform" | "zipf"
     num_shared_experts: int = 0  # 0 or 1: a shared expert on shard local_rank's own tokens
-    weight_format: str = "fp8"   # "fp8" (128x128 block scales) | "mxfp4" (e2m1, UE8M0 per 32 along K)
+    weight_format: str = "fp8"   # "fp8" (128x128 block scales) | "mxfp4" (e2m1, UE8M0 per 32 along K) | "bf16"
     zipf_alpha: float = 1.2
     seed: int = 0
 
@@ -141,6 +141,9 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
     weight_format "mxfp4": w1 [E_w,2I,H/2] and w2 [E_w,H,I/2] hold two e2m1 codes per byte, and w1_sf
     [E_w,2I,H/32] / w2_sf [E_w,H,I/32] hold UE8M0 exponents (uint8) of each 32 values along K.
 
+    weight_format "bf16" (BF16 x BF16): x [S,T,H], w1 [E_w,2I,H] and w2 [E_w,H,I] are bfloat16 and there
+    are no scales (x_sf, w1_sf and w2_sf are None).
+
     integer_codes=True draws every FP8 code from the integers -8..8 and every scale as
     one shared power of two (2^-4 for activations, 2^-6 for weights), so that every
     product and every partial sum of the GEMMs is exact in fp32.  With weight_format "mxfp4"
@@ -164,7 +167,19 @@ def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None,
         hi = torch.randint(0, 16, shape_, generator=gen, device=device)
         return (lo | (hi << 4)).to(torch.uint8)
 
-    if integer_codes and shape.weight_format == "mxfp4":
+    def bf16_ints(shape_):
+        return torch.randint(-8, 9, shape_, generator=gen, device=device).to(torch.bfloat16)
+
+    if shape.weight_format == "bf16":
+        # integer_codes: integers -8..8, exact in bf16, whose GEMM sums stay exact in fp32
+        if integer_codes:
+            x, w1, w2 = bf16_ints((S, T, H)), bf16_ints((El, 2 * I, H)), bf16_ints((El, H, I))
+        else:
+            x = torch.randn((S, T, H), generator=gen, device=device).to(torch.bfloat16)
+            w1 = (torch.randn((El, 2 * I, H), generator=gen, device=device) * 0.02).to(torch.bfloat16)
+            w2 = (torch.randn((El, H, I), generator=gen, device=device) * 0.02).to(torch.bfloat16)
+        x_sf = w1_sf = w2_sf = None
+    elif integer_codes and shape.weight_format == "mxfp4":
         x = ints((S, T, H))
         x_sf = torch.full((S, T, H // 128), 2.0 ** -4, device=device)
         w1 = fp4_codes((El, 2 * I, H // 2))
@@ -218,7 +233,11 @@ def to_numpy(inputs: Dict[str, object]) -> Dict[str, object]:
     """Host (numpy) copies of an input set, for the CPU oracle."""
     out = {}
     for k, v in inputs.items():
-        out[k] = v.detach().cpu().numpy() if isinstance(v, torch.Tensor) else v
+        if isinstance(v, torch.Tensor):
+            v = v.detach().cpu()
+            out[k] = (v.float() if v.dtype == torch.bfloat16 else v).numpy()    # bf16 values exactly
+        else:
+            out[k] = v
     return out
 
 

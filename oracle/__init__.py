@@ -33,5 +33,5 @@ printed on the pages, closed forms, invariants, library routines and brute force
 from .fp8 import (e4m3fn_decode, e4m3fn_encode, bf16_round, bf16_bits)  # noqa: F401
 from .fp4 import (e2m1_decode, e8m0_decode, unpack_fp4, dequant_mx)  # noqa: F401
 from .layer import (route, pool_offsets, rr_inverse, rr_position, rr_sequence,  # noqa: F401
-                    fill_pool, dequant_rows, dequant_blocks, expert_ffn_rows, swiglu,
+                    fill_pool, dequant_rows, dequant_blocks, expert_ffn_rows, expert_ffn_rows_bf16, swiglu,
                     requant_rows, forward, direct_token, ffn_dequantised, dequant_weight, RouteResult)

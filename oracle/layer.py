@@ -174,8 +174,9 @@ def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, to
     if shared_shard is not None:
         off = np.append(off, off[-1] + (int(shared_tokens) + block_m - 1) // block_m)
     P = int(off[-1]) * block_m
-    pool_x = np.zeros((P, H), dtype=np.uint8)
-    pool_sf = np.zeros((P, H // 128), dtype=np.float32)
+    # FP8 codes (uint8) with scales, or (BF16 x BF16, x_sf None) the bf16 values themselves
+    pool_x = np.zeros((P, H), dtype=x.dtype)
+    pool_sf = np.zeros((P, H // 128), dtype=np.float32) if x_sf is not None else None
     pool_meta = np.full((P, 3), META_PAD, dtype=np.uint32)
     for le in range(El):
         base = int(off[le]) * block_m
@@ -188,7 +189,8 @@ def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, to
         t, k = v // topk, v % topk
         rows = base + np.arange(len(seq))
         pool_x[rows] = x[s, t]
-        pool_sf[rows] = x_sf[s, t]
+        if x_sf is not None:
+            pool_sf[rows] = x_sf[s, t]
         pool_meta[rows, 0] = s
         pool_meta[rows, 1] = t
         pool_meta[rows, 2] = k
@@ -196,7 +198,8 @@ def fill_pool(x: np.ndarray, x_sf: np.ndarray, rt: RouteResult, block_m: int, to
         t = np.arange(int(shared_tokens), dtype=np.int64)
         rows = int(off[El]) * block_m + t
         pool_x[rows] = x[shared_shard, t]
-        pool_sf[rows] = x_sf[shared_shard, t]
+        if x_sf is not None:
+            pool_sf[rows] = x_sf[shared_shard, t]
         pool_meta[rows, 0] = shared_shard
         pool_meta[rows, 1] = t
         pool_meta[rows, 2] = topk
@@ -262,6 +265,26 @@ def dequant_weight(codes: np.ndarray, sf: np.ndarray) -> np.ndarray:
     return dequant_blocks(codes, sf)
 
 
+def expert_ffn_rows_bf16(a, w1, w2, intermediate: int, return_parts: bool = False):
+    """One expert's FFN with BF16 x BF16 operands: GEMM1 -> SwiGLU -> bf16 -> GEMM2 -> bf16.
+
+    The pages select a separate BF16 kernel by the operand type, and its input buffer takes the
+    bf16 tokens without scale factors ("DeepGEMM Mega MoE symmetric memory deep analysis", 5.3 and
+    10.1).  Reading taken here (the pages give no detail): the sums are exact (fp64 here, fp32 in
+    the kernel), the SwiGLU output is rounded to bf16 where the FP8 path requantises (the second
+    GEMM's operands are then bf16 as well), and GEMM2's output is cast to bf16 for the combine buffer
+    as in the FP8 path (same page, 8.1-8.2).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    g = a @ np.asarray(w1, dtype=np.float64).T
+    h = swiglu(g, intermediate)
+    hb = bf16_round(h)
+    o = bf16_round(hb @ np.asarray(w2, dtype=np.float64).T)
+    if return_parts:
+        return o, dict(g=g, h=h, l2=hb)
+    return o
+
+
 def expert_ffn_rows(a_codes, a_sf, w1_codes, w1_sf, w2_codes, w2_sf, intermediate: int,
                     gran: int = 128, return_parts: bool = False):
     """One expert's FFN on pooled rows: GEMM1 -> SwiGLU -> FP8 requant -> GEMM2 -> bf16.
@@ -270,8 +293,10 @@ def expert_ffn_rows(a_codes, a_sf, w1_codes, w1_sf, w2_codes, w2_sf, intermediat
     pages ("Mega-MoE notes, part 2", 5.2) is the blockwise form of exactly this sum.
     GEMM2 (down): O = requant(h) W2^T.  The second layer's epilogue casts to bf16 before
     the scatter into the combine buffer ("DeepGEMM Mega MoE symmetric memory deep
-    analysis", 8.1-8.2).
+    analysis", 8.1-8.2).  Rows without scales (a_sf None) are BF16 x BF16: expert_ffn_rows_bf16.
     """
+    if a_sf is None:
+        return expert_ffn_rows_bf16(a_codes, w1_codes, w2_codes, intermediate, return_parts)
     a = dequant_rows(a_codes, a_sf)
     w1 = dequant_weight(w1_codes, w1_sf)
     g = a @ w1.T
@@ -299,6 +324,20 @@ def dequant_rows_gran(codes, sf, gran):
 
 
 # ----------------------------------------------------------------------------- full layer
+def _intermediate(inp) -> int:
+    """I from the down weights: their scales' K extent (FP8: per 128, MXFP4: per 32), or with
+    BF16 x BF16 weights (no scales) the weights' own last axis."""
+    s2 = inp.get("w2_sf")
+    if s2 is None:
+        return int(inp["w2"].shape[2])
+    return int(s2.shape[2] * (32 if s2.dtype == np.uint8 else 128))
+
+
+def _scale_of(inp):
+    """name, expert -> that expert's scale array, or None without scales (BF16 x BF16)."""
+    return lambda name, le: None if inp.get(name) is None else inp[name][le]
+
+
 def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, local_rank: int,
             block_m: int, gran: int = 128, experts: Optional[Sequence[int]] = None,
             keep_rows: bool = False, num_shared_experts: int = 0) -> Dict[str, object]:
@@ -321,12 +360,13 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
     the extra shared slot K, and the shared expert's epilogue applies no routing weight
     ("DeepGEMM Mega MoE symmetric memory deep analysis", 8.1-8.2 and 9.2).
     """
-    x, x_sf = inp["x"], inp["x_sf"]
+    x, x_sf = inp["x"], inp.get("x_sf")
     idx, w = inp["topk_idx"], inp["topk_weights"]
     tps = inp["tokens_per_shard"]
     S, T_max, K = idx.shape
     H = x.shape[2]
-    I = inp["w2_sf"].shape[2] * (32 if inp["w2_sf"].dtype == np.uint8 else 128)
+    I = _intermediate(inp)
+    sf = _scale_of(inp)
     rt = route(idx, tps, num_experts, num_local_experts, local_rank)
     shared = num_shared_experts > 0
     pool_x, pool_sf, pool_meta, off = fill_pool(x, x_sf, rt, block_m, K,
@@ -342,8 +382,8 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
             continue
         base = int(off[le]) * block_m
         rows = slice(base, base + n)
-        o, parts = expert_ffn_rows(pool_x[rows], pool_sf[rows], inp["w1"][le], inp["w1_sf"][le],
-                                   inp["w2"][le], inp["w2_sf"][le], I, gran, return_parts=True)
+        o, parts = expert_ffn_rows(pool_x[rows], None if pool_sf is None else pool_sf[rows], inp["w1"][le],
+                                   sf("w1_sf", le), inp["w2"][le], sf("w2_sf", le), I, gran, return_parts=True)
         meta = pool_meta[rows]
         s_, t_, k_ = meta[:, 0].astype(np.int64), meta[:, 1].astype(np.int64), meta[:, 2].astype(np.int64)
         # combine: accumulate w * comb row into the token's output (each (s,t,k) occurs once)
@@ -354,8 +394,8 @@ def forward(inp: Dict[str, object], num_experts: int, num_local_experts: int, lo
     if shared and int(tps[local_rank]) > 0:
         El, n = num_local_experts, int(tps[local_rank])
         rows = slice(int(off[El]) * block_m, int(off[El]) * block_m + n)
-        o, parts = expert_ffn_rows(pool_x[rows], pool_sf[rows], inp["w1"][El], inp["w1_sf"][El],
-                                   inp["w2"][El], inp["w2_sf"][El], I, gran, return_parts=True)
+        o, parts = expert_ffn_rows(pool_x[rows], None if pool_sf is None else pool_sf[rows], inp["w1"][El],
+                                   sf("w1_sf", El), inp["w2"][El], sf("w2_sf", El), I, gran, return_parts=True)
         y[local_rank, :n] += o
         if keep_rows:
             rows_out[El] = o
@@ -382,9 +422,10 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
     """
     K = inp["topk_idx"].shape[2]
     lo = local_rank * num_local_experts
-    I = inp["w2_sf"].shape[2] * (32 if inp["w2_sf"].dtype == np.uint8 else 128)
+    I = _intermediate(inp)
+    sf = _scale_of(inp)
     a_codes = inp["x"][s, t][None, :]
-    a_sf = inp["x_sf"][s, t][None, :]
+    a_sf = None if inp.get("x_sf") is None else inp["x_sf"][s, t][None, :]
     acc = np.zeros(inp["x"].shape[2], dtype=np.float64)
     slots = []
     for k in range(K):
@@ -394,9 +435,9 @@ def direct_token(inp: Dict[str, object], s: int, t: int, num_local_experts: int,
     if num_shared_experts > 0 and s == local_rank:
         slots.append((num_local_experts, 1.0))
     for le, wk in slots:
-        if cache is None:
-            o = expert_ffn_rows(a_codes, a_sf, inp["w1"][le], inp["w1_sf"][le], inp["w2"][le],
-                                inp["w2_sf"][le], I, gran)[0]
+        if cache is None or a_sf is None:
+            o = expert_ffn_rows(a_codes, a_sf, inp["w1"][le], sf("w1_sf", le), inp["w2"][le],
+                                sf("w2_sf", le), I, gran)[0]
         else:
             if le not in cache:
                 cache[le] = (dequant_weight(inp["w1"][le], inp["w1_sf"][le]),
