@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
 WORKLOAD_TEXT = {
@@ -46,10 +47,12 @@ def algorithmic(shape, R, N, shared_rows=0):
         # route: read every (token, k) expert id, write one table entry per routed pair
         route_bytes=N * K * 8 + R * 4,
         # fill: read the row and its scales, write them and 12 B of metadata, read the table entry
-        fill_bytes=R * (2 * H + 2 * (H // 128) * 4 + 12 + 4),
+        # (BF16 x BF16: rows of 2H bytes and no scales)
+        fill_bytes=R * (4 * H + 12 + 4) if shape.weight_format == "bf16" else R * (2 * H + 2 * (H // 128) * 4 + 12 + 4),
         # combine: read each routed pair's bf16 row, read K ids + weights per token, write the bf16 row
         combine_bytes=R * 2 * H + N * (2 * H + K * 12),
         weight_bytes=(El * 3 * H * I // 2 + El * 3 * H * I // 32) if shape.weight_format == "mxfp4" else
+                     El * 3 * H * I * 2 if shape.weight_format == "bf16" else
                      El * 3 * H * I + El * (2 * I // 128) * (H // 128) * 4 + El * (H // 128) * (I // 128) * 4,
     )
 
@@ -98,9 +101,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-m", type=int, default=None, choices=(64, 128),
                     help="override the workload's BLOCK_M")
-    ap.add_argument("--weight-format", default="fp8", choices=("fp8", "mxfp4"),
-                    help="expert weights: FP8 with 128x128 block scales (the workloads' format) or MXFP4 "
-                         "(e2m1 with UE8M0 exponents per 32 K; the FP8 x FP4 variant)")
+    ap.add_argument("--weight-format", default="fp8", choices=("fp8", "mxfp4", "bf16"),
+                    help="expert weights: FP8 with 128x128 block scales (the workloads' format), MXFP4 "
+                         "(e2m1 with UE8M0 exponents per 32 K; the FP8 x FP4 variant) or BF16 (bf16 tokens "
+                         "and weights, no scales; the BF16 x BF16 variant, timed against the BF16 MFMA peak)")
     ap.add_argument("--shared-experts", type=int, default=0, choices=(0, 1),
                     help="add a shared expert on the own shard's tokens (pool segment + combine slot K)")
     ap.add_argument("--graph", action="store_true",
@@ -227,6 +231,8 @@ def main():
     g1_tflops = g1_flop / (st["gemm1"] * 1e-3) / 1e12
     g2_tflops = 0.0 if one else w["gemm2_flop"] / (st["gemm2"] * 1e-3) / 1e12
     gemm_tflops = (w["gemm1_flop"] + w["gemm2_flop"]) / ((st["gemm1"] + st["gemm2"]) * 1e-3) / 1e12
+    bf16 = shape.weight_format == "bf16"
+    peak = BF16_PEAK_TFLOPS if bf16 else FP8_PEAK_TFLOPS     # the contraction's own dtype
     gbs = lambda b, t: b / (t * 1e-3) / 1e9  # noqa: E731
     fill_stage = ({"schedule": "inside the gemm1 launch (per-block arrival counts); timed with gemm1"} if fused
                   else {"GB/s": gbs(w["fill_bytes"], st["fill"]),
@@ -242,22 +248,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 x fp4" if shape.weight_format == "mxfp4" else "fp8",
+        "dtype": "fp8 x fp4" if shape.weight_format == "mxfp4" else "bf16" if bf16 else "fp8",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload] + (
-                       ", weights MXFP4 (e2m1, UE8M0 per 32 K)" if shape.weight_format == "mxfp4" else "") + (
+                       ", weights MXFP4 (e2m1, UE8M0 per 32 K)" if shape.weight_format == "mxfp4" else
+                       ", BF16 x BF16 (bf16 tokens and weights, no scales)" if bf16 else "") + (
                        f", plus a shared expert on shard {shape.local_rank}'s {shared_rows} tokens"
                        if shape.num_shared_experts else ""), "routed_rows": R, "tokens": N,
                    "parallelism": "one GPU's EP share, source ranks emulated as shards",
                    "routed_rows_per_local_expert": rows_per_expert},
-        "gemm_pct_fp8_peak": 100.0 * gemm_tflops / FP8_PEAK_TFLOPS,
+        ("gemm_pct_bf16_peak" if bf16 else "gemm_pct_fp8_peak"): 100.0 * gemm_tflops / peak,
         "gemm_tflops": gemm_tflops,
         "roofline": {"bound": "mfma",
                      "kernel": "gemm1 (" + ("routing + " if routed_in else "") + ("pool fill + " if fused else "") +
-                               "gate_up + SwiGLU + requant" +
+                               ("gate_up + SwiGLU + bf16" if bf16 else "gate_up + SwiGLU + requant") +
                                (" + down GEMM + scatter, one launch" if one else "") + ")",
-                     "achieved": g1_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": g1_tflops / FP8_PEAK_TFLOPS,
+                     "achieved": g1_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": g1_tflops / peak,
                      "traffic": measured_traffic(args.workload) if default_config else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic": ("6" if one else "4") + "*R*H*I flop per launch, R = routed rows"},
@@ -271,9 +278,9 @@ def main():
             "route": ({"schedule": "inside the gemm1 launch (device-wide barriers); timed with gemm1"} if routed_in
                       else {"GB/s": gbs(w["route_bytes"], st["route"])}),
             "fill": fill_stage,
-            "gemm1": {"TFLOP/s": g1_tflops, "frac": g1_tflops / FP8_PEAK_TFLOPS},
+            "gemm1": {"TFLOP/s": g1_tflops, "frac": g1_tflops / peak},
             "gemm2": ({"schedule": "inside the gemm1 launch (per-block GEMM1 counts); timed with gemm1"} if one
-                      else {"TFLOP/s": g2_tflops, "frac": g2_tflops / FP8_PEAK_TFLOPS}),
+                      else {"TFLOP/s": g2_tflops, "frac": g2_tflops / peak}),
             "combine": {"GB/s": gbs(w["combine_bytes"], st["combine"]),
                         "hbm_frac": gbs(w["combine_bytes"], st["combine"]) / HBM_PEAK_GBS},
             "weights_stream_GB/s": gbs(w["weight_bytes"], st["gemm1"] + st["gemm2"]),

@@ -47,6 +47,8 @@ FLAG_ROUTE_IN_LAUNCH = 0x40
 
 WEIGHTS_FP8 = 0
 WEIGHTS_MXFP4 = 1
+WEIGHTS_BF16 = 2
+_WEIGHT_FORMATS = {"fp8": WEIGHTS_FP8, "mxfp4": WEIGHTS_MXFP4, "bf16": WEIGHTS_BF16}
 
 STAGE_ROUTE = 0x1
 STAGE_FILL = 0x2
@@ -272,7 +274,7 @@ class MegaMoE:
         return cls(shape.num_shards, shape.max_tokens_per_shard, shape.hidden, shape.intermediate,
                    shape.num_experts, shape.num_local_experts, shape.topk, shape.block_m, shape.local_rank,
                    flags, getattr(shape, "num_shared_experts", 0),
-                   WEIGHTS_MXFP4 if getattr(shape, "weight_format", "fp8") == "mxfp4" else WEIGHTS_FP8, **kw)
+                   _WEIGHT_FORMATS[getattr(shape, "weight_format", "fp8")], **kw)
 
     def close(self):
         if self.h is not None:
@@ -290,14 +292,20 @@ class MegaMoE:
         c = self.cfg
         S, T, H, I, El, K = (c.num_shards, c.max_tokens_per_shard, c.hidden, c.intermediate,
                              c.num_local_experts + c.num_shared_experts, c.topk)
-        want = [("x", x, (S, T, H), torch.uint8), ("x_sf", x_sf, (S, T, H // 128), torch.float32),
-                ("topk_idx", topk_idx, (S, T, K), torch.int64),
+        bf16 = c.weight_format == WEIGHTS_BF16
+        want = [("x", x, (S, T, H), torch.bfloat16 if bf16 else torch.uint8)]
+        if not bf16:
+            want += [("x_sf", x_sf, (S, T, H // 128), torch.float32)]
+        want += [("topk_idx", topk_idx, (S, T, K), torch.int64),
                 ("topk_weights", topk_weights, (S, T, K), torch.float32),
                 ("w1 (packed)", w1, self.packed_shapes()[0], torch.uint8),
                 ("w2 (packed)", w2, self.packed_shapes()[1], torch.uint8)]
         if c.weight_format == WEIGHTS_MXFP4:
             s1, s2 = self.packed_scale_shapes()
             want += [("w1_sf (packed)", w1_sf, s1, torch.uint8), ("w2_sf (packed)", w2_sf, s2, torch.uint8)]
+        elif bf16:
+            if x_sf is not None or w1_sf is not None or w2_sf is not None:
+                raise ValueError("BF16 x BF16 takes no scales (x_sf, w1_sf, w2_sf must be None)")
         else:
             want += [("w1_sf", w1_sf, (El, 2 * I // 128, H // 128), torch.float32),
                      ("w2_sf", w2_sf, (El, H // 128, I // 128), torch.float32)]
@@ -313,6 +321,8 @@ class MegaMoE:
         """Shapes of the packed W1 and W2 (see mega_moe_pack_weights)."""
         c = self.cfg
         El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
+        if c.weight_format == WEIGHTS_BF16:                        # 128-byte K chunks of 64 values
+            return (El, I // 128, H // 64, 256, 128), (El, H // 256, I // 64, 256, 128)
         rb = 64 if c.weight_format == WEIGHTS_MXFP4 else 128     # bytes per row and 128-value K step
         return (El, I // 128, H // 128, 256, rb), (El, H // 256, I // 128, 256, rb)
 
@@ -337,15 +347,16 @@ class MegaMoE:
         return p1, p2
 
     def pack_weights(self, w1, w2, stream=None):
-        """Row-major W1 [E_w,2I,H] and W2 [E_w,H,I] (uint8 e4m3fn; E_w = E_l + shared experts, the shared
-        expert last) -> new packed tensors (w1p, w2p)."""
+        """Row-major W1 [E_w,2I,H] and W2 [E_w,H,I] (uint8 e4m3fn, or bfloat16 with BF16 weights; E_w = E_l +
+        shared experts, the shared expert last) -> new packed tensors (w1p, w2p)."""
         import torch
         c = self.cfg
         El, H, I = c.num_local_experts + c.num_shared_experts, c.hidden, c.intermediate
         d = 2 if c.weight_format == WEIGHTS_MXFP4 else 1          # two e2m1 codes per byte
+        dt = torch.bfloat16 if c.weight_format == WEIGHTS_BF16 else torch.uint8
         for name, t, shape in (("w1", w1, (El, 2 * I, H // d)), ("w2", w2, (El, H, I // d))):
-            if tuple(t.shape) != shape or t.dtype != torch.uint8 or not t.is_contiguous() or t.device.type != "cuda":
-                raise ValueError(f"{name}: want contiguous cuda uint8 {shape}, got {t.dtype} {tuple(t.shape)}")
+            if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"{name}: want contiguous cuda {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
         s1, s2 = self.packed_shapes()
         w1p = torch.empty(s1, dtype=torch.uint8, device=w1.device)
         w2p = torch.empty(s2, dtype=torch.uint8, device=w2.device)
@@ -371,12 +382,12 @@ class MegaMoE:
         inputs["w1_sf_packed"] / inputs["w2_sf_packed"]."""
         if "w1_packed" not in inputs or "w2_packed" not in inputs:
             inputs["w1_packed"], inputs["w2_packed"] = self.pack_weights(inputs["w1"], inputs["w2"], stream)
-        s1, s2 = inputs["w1_sf"], inputs["w2_sf"]
+        s1, s2 = inputs.get("w1_sf"), inputs.get("w2_sf")
         if self.cfg.weight_format == WEIGHTS_MXFP4:
             if "w1_sf_packed" not in inputs or "w2_sf_packed" not in inputs:
                 inputs["w1_sf_packed"], inputs["w2_sf_packed"] = self.pack_scales(s1, s2, stream)
             s1, s2 = inputs["w1_sf_packed"], inputs["w2_sf_packed"]
-        return self.forward(inputs["tokens_per_shard"], inputs["x"], inputs["x_sf"], inputs["topk_idx"],
+        return self.forward(inputs["tokens_per_shard"], inputs["x"], inputs.get("x_sf"), inputs["topk_idx"],
                             inputs["topk_weights"], inputs["w1_packed"], s1, inputs["w2_packed"],
                             s2, y, cum_recv_stats, stream, stages)
 

@@ -1,4 +1,4 @@
-// Pool fill: the receiver-side pull of routed FP8 rows into the expert-major L1 pool.
+// Pool fill: the receiver-side pull of routed FP8 (or BF16) rows into the expert-major L1 pool.
 //
 // The routing stage already resolved every pool row to its source: the round-robin position of each
 // index-table entry ("Mega-MoE notes, part 2: index table and pull", 2.5) gave the row's metadata
@@ -33,8 +33,11 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
     const int wave0 = __builtin_amdgcn_readfirstlane(blockIdx.x * (kFillThreads / 64) + (threadIdx.x >> 6));
     const int nwaves = gridDim.x * (kFillThreads / 64);
     const int rows = min((int)p.status[1], p.max_blocks) * p.BM;
-    const int H16 = p.H >> 4;
-    const int SF = p.H >> 7;
+    // bytes per row: H e4m3fn codes, or (BF16 x BF16) H bf16 values, in 128-byte K chunks either way
+    const bool bf16 = p.wfmt == MEGA_MOE_WEIGHTS_BF16;
+    const int Hb = bf16 ? 2 * p.H : p.H;
+    const int H16 = Hb >> 4;
+    const int CH = Hb >> 7;                   // 128-byte chunks per row
     const int J = (H16 + 63) >> 6;            // chunks per lane
     const uint32_t kstride16 = (uint32_t)p.BM * 128;   // bytes between K blocks of the tiled pool
     // chunk c of a row: source byte c*16; tiled destination byte (c/8)*BM*128 + (c%8)*16
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
             const int row = wave0 + (it0 + it) * nwaves;
             const uint32_t src = __builtin_amdgcn_readlane(ms, it), tok = __builtin_amdgcn_readlane(mt, it);
             const int b = row / p.BM, i_in = row - b * p.BM;
-            char* dbase = reinterpret_cast<char*>(p.pool_x + (size_t)b * SF * p.BM * 128 + (size_t)i_in * 128);
+            char* dbase = reinterpret_cast<char*>(p.pool_x + (size_t)b * CH * p.BM * 128 + (size_t)i_in * 128);
             const bool pad = src == kMetaPad;
             if (pad || src >= (uint32_t)p.S || tok >= (uint32_t)p.T_max) {
                 // a non-padding row outside the shards never comes from the routing stage
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
                 continue;
             }
             const size_t srow = (size_t)src * p.T_max + tok;
-            const char* sbase = reinterpret_cast<const char*>(p.x + srow * p.H);
+            const char* sbase = reinterpret_cast<const char*>(p.x + srow * Hb);
             for (int j0 = 0; j0 < J; j0 += kUnroll) {
                 v4i r[kUnroll];
 #pragma unroll
@@ -92,6 +95,8 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
     // values over SF lines).  Padding rows and rows the copy above rejected get zeros.
     // When there are fewer rows than waves (decode) the groups go to the first waves that copy no rows,
     // so the scale pass does not queue behind a row copy.
+    if (bf16) return;                       // no scales
+    const int SF = p.H >> 7;
     const int ngroups = rows >> 6;          // BM is a multiple of 64
     const int first = rows < nwaves ? rows : 0;
     for (int grp = (wave0 - first + nwaves) % nwaves; grp < ngroups; grp += nwaves) {
@@ -124,7 +129,8 @@ hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream) {
     const long max_grid = (long)num_cus * 8;
     if (grid > max_grid) grid = max_grid;
     if (grid < 1) grid = 1;
-    if (p.H % 1024 == 0) hipLaunchKernelGGL(fill_kernel<true>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
+    const int Hb = p.wfmt == MEGA_MOE_WEIGHTS_BF16 ? 2 * p.H : p.H;    // bytes per row
+    if (Hb % 1024 == 0) hipLaunchKernelGGL(fill_kernel<true>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
     else hipLaunchKernelGGL(fill_kernel<false>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
     return hipGetLastError();
 }

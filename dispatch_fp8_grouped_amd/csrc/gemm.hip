@@ -58,6 +58,15 @@ __device__ __forceinline__ v4f mfma_fp4w(const v4i& a, const v8i& b, uint32_t sa
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, b, c, 4, 0, 0, (int)sa, 0, 127);
 }
 
+// BF16 x BF16: a 32-byte fragment (16 bf16 values of lane group g's K range) feeds two 16x16x32 MFMAs,
+// its first and second 16 bytes; both operands split alike, so their K indices pair up.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma_bf16_pair(const v8i& a, const v8i& b, v4f c) {
+    const v4i a0 = __builtin_shufflevector(a, a, 0, 1, 2, 3), a1 = __builtin_shufflevector(a, a, 4, 5, 6, 7);
+    const v4i b0 = __builtin_shufflevector(b, b, 0, 1, 2, 3), b1 = __builtin_shufflevector(b, b, 4, 5, 6, 7);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v8bf, b0), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v8bf, b1), c, 0, 0, 0);
+}
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // scale operands 0 select the unscaled v_mfma_f32_16x16x128_f8f6f4; format 0 = FP8 e4m3
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -410,7 +419,8 @@ enum { kWaitNone = 0, kWaitFill = 1, kWaitGemm1 = 2 };
 // (two e2m1 codes per byte, 64-byte rows per K step, UE8M0 exponents per 32 K applied by the MFMA's
 // scale operand).  kWait: what a tile waits for before its first load.  kPublish (GEMM1): after a
 // tile's stores have completed, count the tile in its block's GEMM1 word.
-template <int BM, int NW, bool kGemm1, bool kStreamW, bool kFp4, int kWait, bool kPublish, bool kXcd>
+template <int BM, int NW, bool kGemm1, bool kStreamW, bool kFp4, int kWait, bool kPublish, bool kXcd,
+          bool kBf16 = false>
 __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan, int nblocks) {
     using Lds = GemmLds<BM, NW, kFp4>;
     auto& sA = Lds::sA();
@@ -449,6 +459,8 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
     static_assert(kGemm1 || kWait != kWaitFill, "the fill feeds GEMM1 only");
     static_assert(kGemm1 || !kPublish, "GEMM1 publishes its tiles");
+    // BF16 x BF16: stream-ordered tiles only; no scales, K steps of 64 values (128 bytes like FP8)
+    static_assert(!kBf16 || (!kFp4 && kWait == kWaitNone && !kPublish && !kXcd), "BF16 schedule");
     constexpr int kStages = GemmLds<BM, NW, kFp4>::kStages;
     constexpr int kInFlight = (kStages - 2) * DMA_PER_STEP;   // at mid-step: the steps after the next one
     static_assert((kStages - 1) * DMA_PER_STEP + kEpiStores < 64, "vmcnt immediate");
@@ -462,7 +474,7 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     const int wm = (wave / NWN) & 1, wn = wave % NWN;
     const int rr = lane & 15, g = lane >> 4;
     const int Kdim = kGemm1 ? p.H : p.I;
-    const int KB = Kdim >> 7;
+    const int KB = kBf16 ? Kdim >> 6 : Kdim >> 7;
     const int NT = kGemm1 ? (p.I >> 7) : (p.H >> 8);
     const int ntiles = (plan.bhi - plan.blo) * NT;
     if (plan.first >= ntiles) return;
@@ -535,9 +547,13 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     // scale j, or (GEMM2) scatter target of row wave*SA_LANES + l; spare lanes, and with MXFP4 weights
     // the two weight-scale lanes, repeat lane 0's load) and the bytes its address advances per K step
     // (token scales are block-major, BM per K block; weight scales K-contiguous)
-    const int sm_role = lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? (kFp4 ? 3 : 1)
+    // (BF16: no scales; every lane loads a scatter target, its own row's in the GEMM2 target lanes and
+    // the wave's first row's otherwise)
+    const int sm_role = kBf16 ? 2 : lane < SA_LANES ? 0 : lane < SA_LANES + 2 ? (kFp4 ? 3 : 1)
                       : (!kGemm1 && lane < 2 * SA_LANES + 2) ? 2 : 3;
-    const int sm_row = wave * SA_LANES + (sm_role == 0 ? lane : sm_role == 2 ? lane - SA_LANES - 2 : 0);
+    const bool tg_row = (unsigned)(lane - SA_LANES - 2) < (unsigned)SA_LANES;
+    const int sm_row = wave * SA_LANES + (kBf16 ? (tg_row ? lane - SA_LANES - 2 : 0)
+                                                : sm_role == 0 ? lane : sm_role == 2 ? lane - SA_LANES - 2 : 0);
     const uint32_t sm_inc = sm_role == 2 ? 0u : sm_role == 1 ? 4u : (uint32_t)(BM * 4);
     const bool sc_lane = lane < SA_LANES;
     const bool ws_lane = !kFp4 && (unsigned)(lane - SA_LANES) < 2u;
@@ -727,15 +743,17 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     auto load_head = [&](Frags& f, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         // (MXFP4: the weight scales are applied inside the MFMA)
-        const float sw0 = kFp4 ? 1.0f : __uint_as_float(sSmall[buf][wave * 64 + SA_LANES]);
-        const float sw1 = kFp4 ? 1.0f : __uint_as_float(sSmall[buf][wave * 64 + SA_LANES + 1]);
+        const float sw0 = kFp4 || kBf16 ? 1.0f : __uint_as_float(sSmall[buf][wave * 64 + SA_LANES]);
+        const float sw1 = kFp4 || kBf16 ? 1.0f : __uint_as_float(sSmall[buf][wave * 64 + SA_LANES + 1]);
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const int r = wm * (BM / 2) + t * 16 + rr;          // token row; loaded by wave r / SA_LANES
             const int slot = (r / SA_LANES) * 64 + r % SA_LANES;
-            const float sa = __uint_as_float(sSmall[buf][slot]);
-            f.sc[0][t] = sa * sw0;
-            if (kGemm1) f.sc[NSW - 1][t] = sa * sw1;
+            if constexpr (!kBf16) {
+                const float sa = __uint_as_float(sSmall[buf][slot]);
+                f.sc[0][t] = sa * sw0;
+                if (kGemm1) f.sc[NSW - 1][t] = sa * sw1;
+            }
             if (!kGemm1) f.dst[kGemm1 ? 0 : t] = sSmall[buf][slot + SA_LANES + 2];
         }
 #pragma unroll
@@ -807,9 +825,30 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
                         *reinterpret_cast<v4f*>(go + (size_t)I * 4 + a * 64) = acc[a + HA][t];
                     }
                 }
+                if constexpr (kBf16) {
+                    // BF16 x BF16: h rounded to bf16 is GEMM2's operand.  The L2 pool holds 64-value K
+                    // blocks as four 16-value quarters of BM rows; this wave's 32 columns of n tile nt
+                    // are K block 2nt + wn/2, quarters 2(wn&1) + a, and the lane's four columns
+                    // 16a + 4g .. +3 are bytes 8g .. 8g+7 of its row's 32 (16 rows x 32 bytes = 512
+                    // contiguous bytes per store instruction)
+#pragma unroll
+                    for (int a = 0; a < HA; ++a) {
+                        const size_t q = ((size_t)b * (I >> 6) + 2 * nt + (wn >> 1)) * 4 + 2 * (wn & 1) + a;
+                        *reinterpret_cast<uint2*>(p.l2_x + (q * BM + wm * (BM / 2) + t * 16) * 32 + lr * 32u + lg * 8u) =
+                            uint2{bf16x2(h[a][t][0], h[a][t][1]), bf16x2(h[a][t][2], h[a][t][3])};
+                    }
+                    continue;
+                }
                 m = fmaxf(m, __shfl_xor(m, 16));
                 m = fmaxf(m, __shfl_xor(m, 32));
                 if (g == 0) sRed[wm * (BM / 2) + t * 16 + rr][wn] = m;
+            }
+            if constexpr (kBf16) {
+#pragma unroll
+                for (int a = 0; a < WN; ++a)
+#pragma unroll
+                    for (int t = 0; t < TM; ++t) acc[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
+                return;
             }
             lds_barrier();
 #pragma unroll
@@ -923,12 +962,18 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
                 issue_dma(ic<buf>{});
                 load_head(fn, ic<(buf + 1) % kStages>{});
             }
-            if constexpr (kFp4) P[i % kRing] = mfma_fp4w(fc.w[i / TM], fc.x[i % TM], fc.ws[i / TM], v4f{0.f, 0.f, 0.f, 0.f});
-            else P[i % kRing] = mfma_fp8(fc.w[i / TM], fc.x[i % TM], v4f{0.f, 0.f, 0.f, 0.f});
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
-            if (i >= kLag) promote(fc, i - kLag);
-            else promote(fn, NMF + i - kLag);                        // previous step's last MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // its promotion on VALU
+            if constexpr (kBf16) {
+                // unscaled operands: the two MFMAs accumulate in place, nothing to promote
+                acc[i / TM][i % TM] = mfma_bf16_pair(fc.w[i / TM], fc.x[i % TM], acc[i / TM][i % TM]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+            } else {
+                if constexpr (kFp4) P[i % kRing] = mfma_fp4w(fc.w[i / TM], fc.x[i % TM], fc.ws[i / TM], v4f{0.f, 0.f, 0.f, 0.f});
+                else P[i % kRing] = mfma_fp8(fc.w[i / TM], fc.x[i % TM], v4f{0.f, 0.f, 0.f, 0.f});
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                if (i >= kLag) promote(fc, i - kLag);
+                else promote(fn, NMF + i - kLag);                    // previous step's last MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // its promotion on VALU
+            }
             if (i < NMF / 2) __builtin_amdgcn_sched_group_barrier(0x100, DS_TAIL, 0);      // LDS reads
             else __builtin_amdgcn_sched_group_barrier(0x100, DS_HEAD, 0);
         }
@@ -940,15 +985,17 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
             for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(acc[a][t]));
         issue_advance((buf + 1) % kStages);
         if (++ckb == KB) {
+            if constexpr (!kBf16) {
 #pragma unroll
-            for (int k = NMF - kLag; k < NMF; ++k) {
-                promote(fc, k);
-                P[k % kRing] = v4f{0.f, 0.f, 0.f, 0.f};   // the next step's catch-up adds zero
+                for (int k = NMF - kLag; k < NMF; ++k) {
+                    promote(fc, k);
+                    P[k % kRing] = v4f{0.f, 0.f, 0.f, 0.f};   // the next step's catch-up adds zero
+                }
+#pragma unroll
+                for (int j = 0; j < NSW; ++j)
+#pragma unroll
+                    for (int t = 0; t < TM; ++t) fc.sc[j][t] = 0.f;
             }
-#pragma unroll
-            for (int j = 0; j < NSW; ++j)
-#pragma unroll
-                for (int t = 0; t < TM; ++t) fc.sc[j][t] = 0.f;
             epilogue(fc);
             ckb = 0;
             ++cj;
@@ -1000,13 +1047,13 @@ __device__ __forceinline__ void load_offsets(const Params& p) {
 // Stream-ordered launch of one GEMM: the tiles of every pool block, spread over all work-groups.  Tiles
 // map XCD-aware: work-group i runs on XCD i mod 8 and takes a run of the tile order with the other
 // work-groups of that XCD.
-template <int BM, int NW, bool kGemm1, bool kStreamW, bool kFp4>
+template <int BM, int NW, bool kGemm1, bool kStreamW, bool kFp4, bool kBf16 = false>
 __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(Params p) {
     const int nblocks = min((int)p.status[1], p.max_blocks);
     const int G = gridDim.x;                    // a multiple of 8
     const TilePlan plan{0, nblocks, (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3), G};
     load_offsets<BM, NW, kFp4>(p);
-    gemm_phase<BM, NW, kGemm1, kStreamW, kFp4, kWaitNone, false, false>(p, plan, nblocks);
+    gemm_phase<BM, NW, kGemm1, kStreamW, kFp4, kWaitNone, false, false, kBf16>(p, plan, nblocks);
 }
 
 // Device-wide barrier: every work-group's writes are released to memory (an L2 writeback) before it
@@ -1134,11 +1181,11 @@ __global__ __launch_bounds__(NW * 64, 1) void xcd_gemm_kernel(Params p) {
     sched_exit(p, nblocks, tid);
 }
 
-template <int BM, bool kGemm1, bool kStreamW = false, bool kFp4 = false>
+template <int BM, bool kGemm1, bool kStreamW = false, bool kFp4 = false, bool kBf16 = false>
 hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     int grid = (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kStreamW, kFp4>), dim3(grid), dim3(kWaves * 64),
-                       0, stream, p);
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, kWaves, kGemm1, kStreamW, kFp4, kBf16>), dim3(grid),
+                       dim3(kWaves * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1158,6 +1205,13 @@ bool weights_stream(const Params& p) { return (double)p.S * p.T_max * p.K / p.E 
 }  // namespace
 
 hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
+    if (p.wfmt == MEGA_MOE_WEIGHTS_BF16) {
+        if (fuse_fill) return hipErrorInvalidConfiguration;   // (refused by the config check)
+        if (p.BM == 64)
+            return weights_stream(p) ? launch<64, true, true, false, true>(p, num_cus, stream)
+                                     : launch<64, true, false, false, true>(p, num_cus, stream);
+        return launch<128, true, false, false, true>(p, num_cus, stream);
+    }
     if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
         if (p.BM == 64)
             return weights_stream(p) ? launch<64, true, true, true>(p, num_cus, stream)
@@ -1173,6 +1227,12 @@ hipError_t launch_gemm1(const Params& p, bool fuse_fill, int num_cus, hipStream_
 }
 
 hipError_t launch_gemm2(const Params& p, int num_cus, hipStream_t stream) {
+    if (p.wfmt == MEGA_MOE_WEIGHTS_BF16) {
+        if (p.BM == 64)
+            return weights_stream(p) ? launch<64, false, true, false, true>(p, num_cus, stream)
+                                     : launch<64, false, false, false, true>(p, num_cus, stream);
+        return launch<128, false, false, false, true>(p, num_cus, stream);
+    }
     if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
         if (p.BM == 64)
             return weights_stream(p) ? launch<64, false, true, true>(p, num_cus, stream)

@@ -66,7 +66,12 @@ int32_t check_config(const mega_moe_config* c) {
     // the shared expert reads the own shard and takes combine slot K (a lane of the combine's ballot)
     if (c->num_shared_experts < 0 || c->num_shared_experts > 1) return MEGA_MOE_ERR_UNSUPPORTED;
     if (c->num_shared_experts && (c->local_rank >= c->num_shards || c->topk >= 64)) return MEGA_MOE_ERR_UNSUPPORTED;
-    if (c->weight_format != MEGA_MOE_WEIGHTS_FP8 && c->weight_format != MEGA_MOE_WEIGHTS_MXFP4)
+    if (c->weight_format != MEGA_MOE_WEIGHTS_FP8 && c->weight_format != MEGA_MOE_WEIGHTS_MXFP4 &&
+        c->weight_format != MEGA_MOE_WEIGHTS_BF16)
+        return MEGA_MOE_ERR_UNSUPPORTED;
+    // BF16 x BF16 runs the stream-ordered kernels only
+    if (c->weight_format == MEGA_MOE_WEIGHTS_BF16 &&
+        (c->flags & (MEGA_MOE_FLAG_FILL_IN_GEMM1 | MEGA_MOE_FLAG_ONE_GEMM_LAUNCH | MEGA_MOE_FLAG_ROUTE_IN_LAUNCH)))
         return MEGA_MOE_ERR_UNSUPPORTED;
     // the arrival-counted fill (and the launch that also routes) is built for FP8 weights only
     if (c->weight_format == MEGA_MOE_WEIGHTS_MXFP4 &&
@@ -113,12 +118,15 @@ void make_layout(const mega_moe_config* c, mega_moe_layout* L) {
     L->block_expert = take(max_blocks * 4);
     L->block_index = take(max_blocks * 4);
     L->table = take(El * S * T * 4);
-    L->pool_x = take(rows * H);
-    L->pool_sf = take(rows * (H / 128) * 4);
+    // BF16 x BF16: pool and L2 pool hold bf16 values (two bytes each) and no scales
+    const bool bf16 = c->weight_format == MEGA_MOE_WEIGHTS_BF16;
+    const uint64_t eb = bf16 ? 2 : 1;
+    L->pool_x = take(rows * H * eb);
+    L->pool_sf = take(bf16 ? 0 : rows * (H / 128) * 4);
     L->pool_meta = take(rows * 3 * 4);
     L->pool_dst = take(rows * 4);
-    L->l2_x = take(rows * I);
-    L->l2_sf = take(rows * (I / 128) * 4);
+    L->l2_x = take(rows * I * eb);
+    L->l2_sf = take(bf16 ? 0 : rows * (I / 128) * 4);
     L->comb = take(((K + nsh) * S * T + 1) * H * 2);   // + one spare row: GEMM2 stores padding rows there
     L->gemm1_out = (c->flags & MEGA_MOE_FLAG_KEEP_GEMM1_OUTPUT) ? take(rows * 2 * I * 4) : 0;
     L->sched = take((mm::kSchedArrival + 2 * max_blocks) * 4);
@@ -168,9 +176,10 @@ int32_t run_forward(const mega_moe_config& c, const mega_moe_layout& L, uint8_t*
     const bool comb = stages & MEGA_MOE_STAGE_COMBINE;
     // pointers each selected stage reads or writes
     auto need = [](bool used, const void* ptr) { return !used || (ptr && aligned16(ptr)); };
-    if (!need(route || comb, a.topk_idx) || !need(fill, a.x) || !need(fill, a.x_sf) || !need(g1, a.w1) ||
-        !need(g1, a.w1_sf) || !need(g2, a.w2) || !need(g2, a.w2_sf) || !need(comb, a.topk_weights) ||
-        !need(comb, a.y))
+    const bool scaled = c.weight_format != MEGA_MOE_WEIGHTS_BF16;     // BF16 x BF16 takes no scales
+    if (!need(route || comb, a.topk_idx) || !need(fill, a.x) || !need(fill && scaled, a.x_sf) ||
+        !need(g1, a.w1) || !need(g1 && scaled, a.w1_sf) || !need(g2, a.w2) || !need(g2 && scaled, a.w2_sf) ||
+        !need(comb, a.topk_weights) || !need(comb, a.y))
         return MEGA_MOE_ERR_INVALID_ARG;
     if (a.cum && ((uintptr_t)a.cum & 3u)) return MEGA_MOE_ERR_INVALID_ARG;
 
@@ -354,9 +363,12 @@ int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const 
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MEGA_MOE_ERR_HIP;
-    if (mm::launch_pack(w1, w2, w1_packed, w2_packed, cfg->num_local_experts + cfg->num_shared_experts, cfg->hidden,
-                        cfg->intermediate, cfg->weight_format == MEGA_MOE_WEIGHTS_MXFP4, cus,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    // BF16 rows are packed as bytes: twice the K bytes of an FP8 row, the same 128-byte K chunks
+    const int kmul = cfg->weight_format == MEGA_MOE_WEIGHTS_BF16 ? 2 : 1;
+    if (mm::launch_pack(w1, w2, w1_packed, w2_packed, cfg->num_local_experts + cfg->num_shared_experts,
+                        cfg->hidden * kmul, cfg->intermediate * kmul, cfg->intermediate,
+                        cfg->weight_format == MEGA_MOE_WEIGHTS_MXFP4, cus, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
         return MEGA_MOE_ERR_HIP;
     return MEGA_MOE_OK;
 }

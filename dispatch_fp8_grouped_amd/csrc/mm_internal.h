@@ -78,7 +78,7 @@ hipError_t launch_gemms(const Params& p, bool fuse_fill, int num_cus, hipStream_
 // Routing, the pull and both GEMMs in one launch (FP8 weights; needs every work-group resident at once)
 hipError_t launch_route_fill_gemms(const Params& p, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
-hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
+hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int Hk, int Ik, int I, bool fp4,
                        int num_cus, hipStream_t stream);
 // MXFP4 exponent transform: [E_w][2I][H/32] / [E_w][H][I/32] bytes -> [E_w][NT][K/128][256] words.
 hipError_t launch_pack_scales(const void* s1, const void* s2, void* s1p, void* s2p, int El, int H, int I,

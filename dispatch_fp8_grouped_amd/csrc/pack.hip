@@ -85,10 +85,14 @@ hipError_t launch_pack_scales(const void* s1, const void* s2, void* s1p, void* s
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int H, int I, bool fp4,
+// Hk / Ik: the K extents of W1 and W2 rows in bytes-per-value units (H and I for FP8 and MXFP4, 2H and
+// 2I for BF16, whose 128-byte K chunks then hold 64 values); I: the intermediate size (W1's gate / up
+// split and W2's row count H = its N extent are in values).  With BF16, W2 has Hk/2 rows.
+hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int El, int Hk, int Ik, int I, bool fp4,
                        int num_cus, hipStream_t stream) {
     const int div = fp4 ? 32 : 16;                  // bytes per weight value: 1/2 or 1
-    const long p1 = (long)El * 2 * I * H / div, p2 = (long)El * H * I / div;
+    const int H = Hk / (Ik / I);                    // W2 rows
+    const long p1 = (long)El * 2 * I * Hk / div, p2 = (long)El * H * Ik / div;
     auto grid = [&](long pieces) { return (unsigned)pack_grid(pieces, num_cus); };
     if (fp4) {
         hipLaunchKernelGGL((pack_kernel<true, 4>), dim3(grid(p1)), dim3(kPackThreads), 0, stream,
@@ -100,11 +104,11 @@ hipError_t launch_pack(const void* w1, const void* w2, void* w1p, void* w2p, int
         return hipGetLastError();
     }
     hipLaunchKernelGGL((pack_kernel<true, 8>), dim3(grid(p1)), dim3(kPackThreads), 0, stream,
-                       static_cast<const v4i*>(w1), static_cast<v4i*>(w1p), 2 * I, H, I, p1);
+                       static_cast<const v4i*>(w1), static_cast<v4i*>(w1p), 2 * I, Hk, I, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((pack_kernel<false, 8>), dim3(grid(p2)), dim3(kPackThreads), 0, stream,
-                       static_cast<const v4i*>(w2), static_cast<v4i*>(w2p), H, I, I, p2);
+                       static_cast<const v4i*>(w2), static_cast<v4i*>(w2p), H, Ik, I, p2);
     return hipGetLastError();
 }
 

@@ -115,6 +115,12 @@ extern "C" {
                                     /* UE8M0 exponent byte per 32 values along K: the FP8 x FP4 variant */
                                     /* of the layer ("DeepGEMM Mega MoE symmetric memory deep analysis", */
                                     /* 10.1-10.2)                                                        */
+#define MEGA_MOE_WEIGHTS_BF16 2     /* BF16 x BF16: bf16 tokens and bf16 weights, no scales: the bf16    */
+                                    /* kernel the pages select by operand type, whose input buffer takes */
+                                    /* the tokens without scale factors ("DeepGEMM Mega MoE symmetric    */
+                                    /* memory deep analysis", 5.3 and 10.1).  The pool, the L2 pool and  */
+                                    /* GEMM1's output (SwiGLU rounded to bf16) hold bf16 values.  Stream-*/
+                                    /* ordered kernels only: the in-launch schedule flags are refused   */
 
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
 #define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */
@@ -148,7 +154,7 @@ typedef struct mega_moe_config {
                                   /* ("DeepGEMM Mega MoE symmetric memory deep analysis", 4.1, 8.1-8.2, */
                                   /* 9.2: the shared expert reads the rank's own input buffer and        */
                                   /* writes the extra combine slot K locally)                           */
-    int32_t weight_format;        /* MEGA_MOE_WEIGHTS_FP8 (default) or MEGA_MOE_WEIGHTS_MXFP4           */
+    int32_t weight_format;        /* MEGA_MOE_WEIGHTS_FP8 (default), _MXFP4 or _BF16                   */
 } mega_moe_config;
 
 /* Byte offsets of the regions inside the workspace (for tests and tools) plus the resolved sizes. */
@@ -173,14 +179,18 @@ typedef struct mega_moe_layout {
     uint64_t pool_x;          /* uint8 [max_pool_blocks][H/128][BM][128] e4m3fn: pool row b*BM+m,  */
                               /*   columns kb*128..+127 at ((b*(H/128) + kb)*BM + m)*128 (tiled, so */
                               /*   one block's K step is one contiguous 16 KB chunk at BM = 128)     */
+                              /*   BF16: the same tiling of 2H bytes per row, [H/64] chunks of 64     */
+                              /*   bf16 values                                                       */
     uint64_t pool_sf;         /* float [max_pool_blocks][H/128][BM]: block-major, so the BM scales */
-                              /*   of one block and K block are contiguous                          */
+                              /*   of one block and K block are contiguous (empty with BF16)         */
     uint64_t pool_meta;       /* uint32 [max_pool_blocks*BM][3] = {shard, token, k}; padding = ~0  */
     uint64_t pool_dst;        /* uint32 [max_pool_blocks*BM]: comb row k*S*T_max + shard*T_max +   */
                               /*   token of the pool row (the GEMM2 scatter target); padding = ~0  */
     uint64_t l2_x;            /* uint8 [max_pool_blocks][I/128][4][BM][32] e4m3fn: per block and K  */
-                              /* block, four 32-column quarters of BM rows                        */
+                              /* block, four 32-column quarters of BM rows.  BF16: bf16            */
+                              /* [max_pool_blocks][I/64][4][BM][16], the same 128-byte K blocks    */
     uint64_t l2_sf;           /* float [max_pool_blocks][I/128][BM], block-major like pool_sf      */
+                              /*   (empty with BF16)                                                 */
     uint64_t comb;            /* bf16 [K + n_shared][S*T_max][H]: rows of routed (k, shard, token) */
                               /* (plane K: the shared expert's rows of the own shard), then one    */
                               /* spare row that takes GEMM2's padding rows                        */
@@ -223,6 +233,9 @@ int32_t mega_moe_init(const mega_moe_config* cfg, void* workspace, uint64_t work
  * With weight_format MEGA_MOE_WEIGHTS_MXFP4 the inputs are the e2m1 codes, uint8 [E_w][2I][H/2] and
  * [E_w][H][I/2], and each packed row holds 64 bytes per K step: w1_packed [E_w][I/128][H/128][256][64],
  * w2_packed [E_w][H/256][I/128][256][64], same row order.
+ * With weight_format MEGA_MOE_WEIGHTS_BF16 the inputs are bf16 [E_w][2I][H] and [E_w][H][I], packed as
+ * bytes with 128-byte (64-value) K chunks: w1_packed [E_w][I/128][H/64][256][128] (chunk (le, nt, kb), row
+ * r, bytes of W1 values kb*64 .. kb*64+63), w2_packed [E_w][H/256][I/64][256][128].
  * Asynchronous on `stream`; no handle is needed.
  * Errors: INVALID_ARG (null or not 16-byte aligned pointer), UNSUPPORTED (config), HIP. */
 int32_t mega_moe_pack_weights(const mega_moe_config* cfg, const void* w1, const void* w2, void* w1_packed,
@@ -258,6 +271,8 @@ int32_t mega_moe_pack_scales(const mega_moe_config* cfg, const void* w1_sf, cons
  *                     With weight_format MEGA_MOE_WEIGHTS_MXFP4: w1 / w2 are the packed e2m1 codes and
  *                     w1_sf / w2_sf the exponents packed by mega_moe_pack_scales (uint8, passed through
  *                     the same float pointers)
+ *                     With weight_format MEGA_MOE_WEIGHTS_BF16: x is bf16 [S][T_max][H], w1 / w2 are packed
+ *                     from bf16 weights, and x_sf, w1_sf, w2_sf are not read (NULL allowed)
  *   y                 bf16 [S][T_max][H] output: y[s,t] = sum over k with a local expert of
  *                     w[s,t,k] * Expert(x[s,t]), plus Shared(x[s,t]) for s = local_rank when the
  *                     config has a shared expert; a token with nothing to add gets a zero row
