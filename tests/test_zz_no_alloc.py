@@ -25,10 +25,10 @@ def _noalloc(shape, inp):
     cfg = moe.cfg
     lib = mm.lib()
     tps = (ctypes.c_int32 * S)(*inp["tokens_per_shard"])
-    p = lambda t: ctypes.c_void_p(t.data_ptr())        # noqa: E731
-    rc = lib.mega_moe_forward_noalloc(ctypes.byref(cfg), tps, p(inp["x"]), p(inp["x_sf"]), p(inp["topk_idx"]),
-                                      p(inp["topk_weights"]), p(inp["w1_packed"]), p(inp["w1_sf"]),
-                                      p(inp["w2_packed"]), p(inp["w2_sf"]), p(y), None, p(status),
+    p = lambda t: ctypes.c_void_p(None if t is None else t.data_ptr())   # noqa: E731
+    rc = lib.mega_moe_forward_noalloc(ctypes.byref(cfg), tps, p(inp["x"]), p(inp.get("x_sf")), p(inp["topk_idx"]),
+                                      p(inp["topk_weights"]), p(inp["w1_packed"]), p(inp.get("w1_sf")),
+                                      p(inp["w2_packed"]), p(inp.get("w2_sf")), p(y), None, p(status),
                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert rc == 0, mm.mega_moe_strerror(rc)
@@ -54,3 +54,11 @@ def test_noalloc_forward_matches_forward_on_two_calls():
     inp = make_inputs(small, device="cuda", tokens_per_shard=[96, 17, 0])
     n2 = _noalloc(small, inp)
     assert n1 > n2 > 0
+
+
+def test_noalloc_forward_matches_forward_bf16():
+    """The same entry point with BF16 x BF16 weights (no scale pointers)."""
+    print("[case] noalloc bf16", flush=True)
+    sh = MoEShape("noalloc_bf16", 3, 96, 512, 256, 16, 8, 4, 64, seed=52, weight_format="bf16")
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=[96, 40, 7])
+    assert _noalloc(sh, inp) > 0
