@@ -5,7 +5,8 @@
 // ("Mega-MoE kernel code walkthrough: from Dispatch to WGMMA", 4.2), which makes the slot order
 // depend on timing.  Here the same counting sort ("Dispatch/Combine: blog theory vs DeepEP vs DeepGEMM
 // Mega MoE", 4.4: count, prefix sum, scatter) is done deterministically: slots of one (expert, shard)
-// follow ascending t*K+k.  Three launches (one, route_small, for inputs whose counts fit in LDS):
+// follow ascending t*K+k.  Three launches (one, route_small, for inputs whose counts fit in LDS; two,
+// with route_count_scan in place of the first two, for shards of at most 8 chunks):
 //   route_count  grid (chunks, S): LDS histogram of one chunk of 256 (token, k) entries over all E
 //   route_scan   grid S:           send[s][e], per-chunk slot bases, recv
 //   route_table  grid (chunks, S), one wave each: the pool offsets from recv ("Mega-MoE notes, part 2:
@@ -28,6 +29,38 @@ __global__ __launch_bounds__(kCountThreads) void route_count_kernel(Params p) {
 
 // One work-group per shard.
 __global__ __launch_bounds__(1024) void route_scan_kernel(Params p) { route_scan_shard(p, blockIdx.x, threadIdx.x, 1024); }
+
+// Counts and scan in one launch, for shards of at most a few chunks (decode): one work-group per shard
+// histograms kFusedChunks chunks at a time (256 threads per chunk, one LDS histogram each), writes them
+// to chunk_hist, and after a barrier (the same work-group reads them back) runs the scan.  Saves the
+// count launch where its 4 us and the launch gap are a tenth of the routing.
+constexpr int kFusedChunks = 4;
+constexpr int kFusedMaxChunks = 8;
+__global__ __launch_bounds__(1024) void route_count_scan_kernel(Params p) {
+    extern __shared__ int hist[];   // [kFusedChunks][E]
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const long n = (long)p.tps[s] * p.K;
+    const int64_t* idx = p.topk_idx + (size_t)s * p.T_max * p.K;
+    bool bad = false;
+    for (int c0 = 0; c0 < p.chunks; c0 += kFusedChunks) {
+        for (int i = tid; i < kFusedChunks * p.E; i += 1024) hist[i] = 0;
+        __syncthreads();
+        const int j = tid / kRouteChunk, c = c0 + j;
+        const long f = (long)c * kRouteChunk + (tid % kRouteChunk);
+        const int64_t e = (c < p.chunks && f < n) ? idx[f] : -1;
+        if (e >= p.E) bad = true;
+        else if (e >= 0) atomicAdd(&hist[j * p.E + (int)e], 1);
+        __syncthreads();
+        for (int i = tid; i < kFusedChunks * p.E; i += 1024) {
+            const int cc = c0 + i / p.E;
+            if (cc < p.chunks) p.chunk_hist[((size_t)s * p.chunks + cc) * p.E + i % p.E] = hist[i];
+        }
+        __syncthreads();
+    }
+    if (bad) atomicOr(p.status, MEGA_MOE_STATUS_BAD_EXPERT_ID);
+    route_scan_shard(p, s, tid, 1024);
+}
+static_assert(kFusedChunks * kRouteChunk == 1024, "one thread per entry of kFusedChunks chunks");
 
 // One wave per (chunk, shard).
 template <bool kRegRun>
@@ -210,10 +243,15 @@ hipError_t launch_route(const Params& p, hipStream_t stream) {
         return hipGetLastError();
     }
     dim3 grid(p.chunks, p.S);
-    hipLaunchKernelGGL(route_count_kernel, grid, dim3(kCountThreads), p.E * sizeof(int), stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(p.S), dim3(1024), 0, stream, p);
+    hipError_t err;
+    if (p.chunks <= kFusedMaxChunks && !(p.flags & MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES)) {
+        hipLaunchKernelGGL(route_count_scan_kernel, dim3(p.S), dim3(1024), kFusedChunks * p.E * sizeof(int), stream, p);
+    } else {
+        hipLaunchKernelGGL(route_count_kernel, grid, dim3(kCountThreads), p.E * sizeof(int), stream, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(route_scan_kernel, dim3(p.S), dim3(1024), 0, stream, p);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (p.El <= 64) hipLaunchKernelGGL(route_table_kernel<true>, grid, dim3(64), 0, stream, p);

@@ -90,8 +90,10 @@ extern "C" {
                                                   this forward wrote it turns the output into NaN (uses
                                                   hipMemsetAsync: not for graph capture) */
 #define MEGA_MOE_FLAG_DEBUG_ROUTE_LAUNCHES 0x20u /* tests: always route with the three-launch kernels, even
-                                                  where the one-work-group routing would be used (at most
-                                                  S*ceil(T_max*K/64) <= 32 groups of 64 entries) */
+                                                  where the one-work-group routing (at most
+                                                  S*ceil(T_max*K/64) <= 32 groups of 64 entries) or the
+                                                  counts and scan in one launch (at most 8 chunks of 256
+                                                  entries per shard) would be used */
 #define MEGA_MOE_FLAG_ROUTE_IN_LAUNCH 0x40u    /* routing, the pull and both GEMMs in one persistent launch
                                                   (FP8 weights; all five stages selected): the routing
                                                   stages run over all work-groups, each ended by a

@@ -264,12 +264,13 @@ def test_stage_timing():
     alls.close()
 
 
-@pytest.mark.parametrize("route", ["one_group", "three_launches"])
+@pytest.mark.parametrize("route", ["default", "three_launches"])
 @pytest.mark.parametrize("case", ["zipf_uneven", "many_shards", "zipf_small"])
 def test_route_stage_places_pool_rows(case, route):
     """The routing stage alone writes every pool row's metadata and scatter target (the round-robin
     position of each table entry, padding rows all ones), over poisoned workspace contents, with the
-    one-work-group routing of small inputs and with the three-launch routing."""
+    routing the library picks (one work-group for zipf_small; counts and scan in one launch for the
+    others, whose shards hold at most 8 chunks) and with the three-launch routing."""
     print(f"[case] route-only pool metadata {case}, routing {route}", flush=True)
     if case == "zipf_uneven":
         sh = MoEShape("rz", 6, 300, 256, 128, 64, 16, 6, 64, local_rank=2, routing="zipf", seed=31)
