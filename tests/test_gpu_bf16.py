@@ -207,3 +207,23 @@ def test_bf16_full_size_decode_sampled_tokens():
         want = oracle.direct_token(n, s, t, sh.num_local_experts, sh.local_rank)
         tol_check(y[s, t], want, f"token ({s},{t})")
     run.close()
+
+
+@pytest.mark.parametrize("case", ["max_hidden", "max_intermediate"])
+def test_bf16_maximum_sizes_whole_layer(case):
+    """The configuration maxima with bf16 operands: H = 16384 (rows of 32 KB, 256 K steps of 64 values in
+    GEMM1, 32 fill chunks per lane) and I = 16384 (256 K steps in GEMM2, 128 GEMM1 n tiles)."""
+    print(f"[case] bf16 maximum sizes {case}", flush=True)
+    if case == "max_hidden":
+        sh = MoEShape("bfmaxh", 2, 24, 16384, 4096, 2, 1, 1, 64, weight_format="bf16", seed=211)
+        tps = [24, 19]
+    else:
+        sh = MoEShape("bfmaxi", 2, 24, 4096, 16384, 2, 1, 1, 64, weight_format="bf16", seed=212)
+        tps = [24, 11]
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    run = Run(sh, inputs=inp)
+    assert run.status == 0
+    n = inputs_np(run)
+    _check_layout_bf16(run, n)
+    _whole(run, n)
+    run.close()
