@@ -123,9 +123,15 @@ __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream) {
-    // Enough waves to cover HBM latency; rows beyond the routed count make the waves exit at once.
+    // Enough waves to cover HBM latency; rows beyond the routed count make the waves exit at once.  The
+    // grid follows the rows expected under uniform routing (each local expert's share padded to BM) with
+    // a 2x margin, not the pool's capacity: at decode that halves the work-groups launched (the layer
+    // 0.302 -> 0.299 ms); the waves loop, so any row count is covered.
     const long cap_rows = (long)p.max_blocks * p.BM;
-    long grid = (cap_rows + 3) / 4;
+    const long per_e = ((long)p.S * p.T_max * p.K / p.E + p.BM - 1) / p.BM * p.BM;
+    const long exp_rows = 2 * per_e * (p.El + p.nsh);
+    long grid = ((exp_rows < cap_rows ? exp_rows : cap_rows) + 3) / 4;
+    if (grid < num_cus) grid = num_cus;
     const long max_grid = (long)num_cus * 8;
     if (grid > max_grid) grid = max_grid;
     if (grid < 1) grid = 1;
