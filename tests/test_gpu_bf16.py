@@ -227,3 +227,48 @@ def test_bf16_maximum_sizes_whole_layer(case):
     _check_layout_bf16(run, n)
     _whole(run, n)
     run.close()
+
+
+def _bf16_sweep(n=16, seed=2031):
+    """Random small BF16 layers: BLOCK_M 64/128, H 256-1024, I 128-512, 1-16 local experts on 1, 2 or 4
+    ranks, top-1..8, 1-4 shards with random (possibly zero) token counts, uniform or Zipf routing, with
+    or without a shared expert."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        bm = int(rng.choice([64, 128]))
+        H = int(rng.choice([256, 512, 768, 1024]))
+        I = int(rng.choice([128, 256, 384, 512]))
+        El = int(rng.integers(1, 17))
+        R = int(rng.choice([1, 2, 4]))
+        E = El * R
+        K = int(rng.integers(1, min(E, 8) + 1))
+        S = int(rng.integers(1, 5))
+        T = int(rng.integers(1, 257))
+        rank = int(rng.integers(0, R))
+        nsh = int(rng.integers(0, 2)) if rank < S else 0
+        routing = "zipf" if rng.random() < 0.3 else "uniform"
+        tps = [int(rng.integers(0, T + 1)) for _ in range(S)]
+        out.append((MoEShape(f"bfsweep{i}", S, T, H, I, E, El, K, bm, local_rank=rank, routing=routing,
+                             num_shared_experts=nsh, weight_format="bf16", seed=600 + i), tps))
+    return out
+
+
+_BF16_SWEEP = _bf16_sweep()
+
+
+@pytest.mark.parametrize("case", range(len(_BF16_SWEEP)), ids=[sh.name for sh, _ in _BF16_SWEEP])
+def test_bf16_random_configs_whole_layer(case):
+    """Each seeded configuration: layout and pool rows bit for bit, the whole output within tolerance,
+    a clean status."""
+    sh, tps = _BF16_SWEEP[case]
+    print(f"[case] bf16 sweep {sh.name} bm={sh.block_m} H={sh.hidden} I={sh.intermediate} "
+          f"E={sh.num_experts}/{sh.num_local_experts} K={sh.topk} tps={tps} shared={sh.num_shared_experts}",
+          flush=True)
+    inp = make_inputs(sh, tokens_per_shard=tps)
+    run = Run(sh, inputs=inp)
+    assert run.status == 0
+    n = inputs_np(run)
+    _check_layout_bf16(run, n)
+    _whole(run, n)
+    run.close()
