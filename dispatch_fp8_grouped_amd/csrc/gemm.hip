@@ -400,6 +400,12 @@ struct GemmLds {
         __shared__ int v[MEGA_MOE_MAX_LOCAL_EXPERTS + 2];
         return v;
     }
+    // the first kTileTab tiles of the work-group's run: {pool block, n tile, local expert, first K block}
+    static constexpr int kTileTab = 128;
+    __device__ __forceinline__ static auto& sTile() {
+        __shared__ __attribute__((aligned(16))) uint4 v[kTileTab];
+        return v;
+    }
 };
 
 // Which pool blocks a work-group's tiles come from, and which of their tiles it takes: tiles first,
@@ -489,7 +495,7 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     // block of one expert: the blocks' A chunks and the n tiles' W chunks are shared through that
     // XCD's L2, each W tile is fetched by one or two XCDs and each A block about NT/4 times.
     auto clip = [&](int i) { return kXcd ? min(max(sOff[i], plan.blo), plan.bhi) - plan.blo : sOff[i]; };
-    auto tile_of = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
+    auto tile_search = [&](int j, int& b, int& nt, int& le) __attribute__((always_inline)) {
         const int t = plan.first + j * plan.stride;
         const int vb = t / NT;
         int lo = 0, hi = nseg;              // the expert with c[le] <= vb < c[le+1]
@@ -502,10 +508,47 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
         const int u = t - b0 * NT;
         nt = u / nb;
         b = plan.blo + b0 + (u - nt * nb);
+    };
+    // The search costs a chain of dependent LDS reads and an integer division, and every wave of the
+    // work-group runs it at the same step of a tile change, so the matrix cores would idle meanwhile.
+    // The work-group's first kTileTab tiles are therefore looked up once here, one tile per thread
+    // (stream-ordered launches; the in-launch schedules have no registers to spare for it).
+    auto& sTile = Lds::sTile();
+    constexpr int kTileTab = kXcd ? 0 : Lds::kTileTab;
+    // The K-start rotation of a tile (kRotate, see the issue side below): its block within the expert
+    // and its n tile give the first K block, jb*kRotJ + nt*kRotN mod KB.
+    auto rot_start = [&](int b, int nt, int le) {
+        int kc = kRotJ * (b - sOff[le]) + kRotN * nt;
+        while (kc >= KB) kc -= KB;
+        return kc;
+    };
+    if constexpr (kTileTab > 0) {
+        for (int j = tid; j < min(my_tiles, kTileTab); j += NW * 64) {
+            int b, nt, le;
+            tile_search(j, b, nt, le);
+            b = min(max(b, 0), nblocks - 1);
+            nt = min(max(nt, 0), NT - 1);
+            sTile[j] = uint4{(uint32_t)b, (uint32_t)nt, (uint32_t)le, (uint32_t)(kRotate ? rot_start(b, nt, le) : 0)};
+        }
+        __syncthreads();
+    }
+    // kc: the tile's first K block when the table holds it, else -1
+    auto tile_of = [&](int j, int& b, int& nt, int& le, int& kc) __attribute__((always_inline)) {
+        if (kTileTab > 0 && (unsigned)j < (unsigned)kTileTab) {
+            const uint4 v = sTile[j];
+            b = (int)v.x;
+            nt = (int)v.y;
+            le = (int)v.z;
+            kc = (int)v.w;
+        } else {
+            tile_search(j, b, nt, le);
+            kc = -1;
+        }
         // wave-uniform by construction; the offsets come from LDS, so say so for the scalar DMA bases
         b = __builtin_amdgcn_readfirstlane(min(max(b, 0), nblocks - 1));   // inconsistent offsets only
         nt = __builtin_amdgcn_readfirstlane(min(max(nt, 0), NT - 1));
         le = __builtin_amdgcn_readfirstlane(le);
+        kc = __builtin_amdgcn_readfirstlane(kc);
     };
     // A (pool or L2 pool) and W (packed weights) are tiled: the K step kb of block b is the contiguous
     // BM x 128 chunk at a_base(b) + kb*BM*128, that of n tile nt of expert le the 256 x 128 chunk at
@@ -588,8 +631,8 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     const uint32_t ws_off = (uint32_t)ws_tr * 4u;
     // landed: the stage whose DMA landed last (-1 in the prologue)
     auto set_issue_tile = [&](int landed) __attribute__((always_inline)) {
-        int b, nt, le;
-        tile_of(ij, b, nt, le);
+        int b, nt, le, kc;
+        tile_of(ij, b, nt, le, kc);
         if constexpr (kWait != kWaitNone) {
             // The tile's block is complete before its first load.  The probe DMA of the steps issued
             // for the previous tile read this block's word: the stage that landed last holds its value
@@ -597,17 +640,12 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
             const bool seen = landed >= 0 && KB >= kStages &&
                               __builtin_amdgcn_readfirstlane(sProbe[landed][wave]) >= wait_target;
             if (__builtin_expect(!seen, 0)) spin_until(p, wait_words + b, wait_target, lane);
-            int bn = b, ntn, len;
-            if (ij + 1 < my_tiles) tile_of(ij + 1, bn, ntn, len);
+            int bn = b, ntn, len, kcn;
+            if (ij + 1 < my_tiles) tile_of(ij + 1, bn, ntn, len, kcn);
             iProbe = static_cast<const uint32_t*>(sgpr_ptr(wait_words + bn));
         }
         const size_t row0 = (size_t)b * BM;
-        if constexpr (kRotate) {
-            const int jb = __builtin_amdgcn_readfirstlane(b - sOff[le]);    // block within its expert
-            int kc = kRotJ * jb + kRotN * nt;          // mod KB on the scalar unit
-            while (kc >= KB) kc -= KB;
-            ikc = kc;
-        }
+        if constexpr (kRotate) ikc = kc >= 0 ? kc : __builtin_amdgcn_readfirstlane(rot_start(b, nt, le));
         iA = static_cast<const uint8_t*>(sgpr_ptr(a_base(b) + (size_t)ikc * BM * 128));
         iW = static_cast<const uint8_t*>(sgpr_ptr(w_base(le, nt) + (size_t)ikc * 256 * WRB));
         if constexpr (kLaneSmall) {
@@ -787,9 +825,10 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
 
     auto epilogue = [&](const Frags& f) __attribute__((always_inline)) {
         // lane holds acc[a][t][i]: weight row wr - rr + wrow(a) + 4g + i, token wm*BM/2 + 16t + rr
-        int b, nt, le_unused;
-        tile_of(cj, b, nt, le_unused);
+        int b, nt, le_unused, kc_unused;
+        tile_of(cj, b, nt, le_unused, kc_unused);
         (void)le_unused;
+        (void)kc_unused;
         const size_t row0 = (size_t)b * BM;
         if (kGemm1) {
             constexpr int HA = WN / 2;
