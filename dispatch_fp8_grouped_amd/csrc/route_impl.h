@@ -176,6 +176,9 @@ __device__ __forceinline__ void route_table_chunk(const Params& p, int c, int s,
         const long f = f0 + r * 64 + lane;
         e_of[r] = f < n ? idx[f] : -1;
     }
+    // (E_l <= 64) the chunk's slot bases, one per lane: issued with the ids, so their latency overlaps
+    int run_reg = 0;
+    if (kRegRun) run_reg = lane < p.El ? base[lane] : 0;
     const bool staged = p.El * p.S <= stage_ints;
     const int* recv_v = p.recv;
     if (staged) {
@@ -199,10 +202,7 @@ __device__ __forceinline__ void route_table_chunk(const Params& p, int c, int s,
     }
     pool_layout(p, recv_v, offs, lane);
     const int* off_v = offs;
-    int run_reg = 0;
-    if (kRegRun) {
-        run_reg = lane < p.El ? base[lane] : 0;
-    } else {
+    if (!kRegRun) {
         for (int le = lane; le < p.El; le += 64) run[le] = base[le];
     }
     wave_lds_sync();
