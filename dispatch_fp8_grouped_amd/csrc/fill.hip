@@ -16,10 +16,6 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kFillThreads = 256;
-#ifndef MM_FILL_UNROLL
-#define MM_FILL_UNROLL 4
-#endif
-constexpr int kUnroll = MM_FILL_UNROLL;   // 16-byte chunks per lane per batch
 
 // Lane l copies chunks l, l+64, ... of a row.  A batch issues kUnroll loads, then kUnroll stores, with
 // no branch between them: indices past the row's end are clamped to its last chunk, so those lanes
@@ -27,7 +23,10 @@ constexpr int kUnroll = MM_FILL_UNROLL;   // 16-byte chunks per lane per batch
 // memory-counter waits exact; a per-lane branch around a load or store makes it wait for every
 // outstanding access, stores included, before each store.
 // kFull: H is a multiple of 1024, so every lane has the same chunk count and no index is clamped.
-template <bool kFull>
+// kUnroll: 16-byte chunks per lane per batch.  Seven when a row is seven chunks per lane (H = 7168: one
+// load round per row, 48 VGPRs, still 8 waves per SIMD; prefill fill 96.5-97.1 -> 93.2-93.5 us in a
+// same-box A/B), else four.
+template <bool kFull, int kUnroll>
 __global__ __launch_bounds__(kFillThreads, 8) void fill_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     const int wave0 = __builtin_amdgcn_readfirstlane(blockIdx.x * (kFillThreads / 64) + (threadIdx.x >> 6));
@@ -136,8 +135,12 @@ hipError_t launch_fill(const Params& p, int num_cus, hipStream_t stream) {
     if (grid > max_grid) grid = max_grid;
     if (grid < 1) grid = 1;
     const int Hb = p.wfmt == MEGA_MOE_WEIGHTS_BF16 ? 2 * p.H : p.H;    // bytes per row
-    if (Hb % 1024 == 0) hipLaunchKernelGGL(fill_kernel<true>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
-    else hipLaunchKernelGGL(fill_kernel<false>, dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
+    const int J = ((Hb >> 4) + 63) >> 6;                                // 16-byte chunks per lane and row
+    if (Hb % 1024 == 0 && J % 7 == 0)
+        hipLaunchKernelGGL((fill_kernel<true, 7>), dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
+    else if (Hb % 1024 == 0)
+        hipLaunchKernelGGL((fill_kernel<true, 4>), dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
+    else hipLaunchKernelGGL((fill_kernel<false, 4>), dim3((unsigned)grid), dim3(kFillThreads), 0, stream, p);
     return hipGetLastError();
 }
 
