@@ -103,3 +103,23 @@ def test_combine_stage_alone_reproduces_weighted_sum():
     assert np.max(np.abs(got[0, 0] - oracle.bf16_round(fp32.astype(np.float64)))) <= \
         2.0 ** -7 * np.max(np.abs(fp32)), "0.73*E2 + 0.27*E7"
     moe.close()
+
+
+def test_tile_runs_longer_than_the_lookup_table():
+    """A GEMM1 launch with more than 128 tiles per work-group (I = 16384: 128 n tiles per pool block,
+    ~264 blocks), so each work-group finds its first 128 tiles in the LDS table and the rest by the
+    search over the expert offsets.  The last expert's tiles come last in the tile order, where the
+    search takes over: every combine row of it against the oracle, and the layout bit for bit."""
+    print("[case] tile runs past the lookup table", flush=True)
+    sh = MoEShape("longrun", 8, 2056, 256, 16384, 8, 8, 1, 64, seed=41)
+    run = Run(sh)
+    assert run.status == 0
+    n = inputs_np(run)
+    rt, _ = check_layout(run, n)
+    nblocks = int(run.layout_host()["nblocks"])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = (cus + 7) // 8 * 8
+    tiles = nblocks * (sh.intermediate // 128)
+    assert tiles > 128 * grid, (tiles, grid)            # some work-groups run past the table
+    _expert_rows(run, n, [sh.num_local_experts - 1])
+    run.close()
