@@ -13,15 +13,23 @@ from gpu_util import Run, check_layout, inputs_np, tol_check
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_whole_output():
-    """The decode-shaped share (8 x 128 tokens, H 7168, I 2048, 32 of 256 experts, BLOCK_M 64): the layout
-    bit for bit and every output row against the oracle."""
-    print("[case] decode whole y", flush=True)
-    sh = SHAPES["decode"]
+@pytest.mark.parametrize("weight_format", ["fp8", "mxfp4", "bf16"])
+def test_decode_whole_output(weight_format):
+    """The decode-shaped share (8 x 128 tokens, H 7168, I 2048, 32 of 256 experts, BLOCK_M 64), with each
+    weight format: the routing counts bit for bit (and, with FP8 or MXFP4 weights, the whole layout) and
+    every output row against the oracle."""
+    print(f"[case] decode whole y, {weight_format} weights", flush=True)
+    sh = SHAPES["decode"].replace(weight_format=weight_format)
     run = Run(sh)
     assert run.status == 0
     n = inputs_np(run)
-    check_layout(run, n)
+    if weight_format == "bf16":
+        rt = oracle.route(n["topk_idx"], n["tokens_per_shard"], sh.num_experts, sh.num_local_experts,
+                          sh.local_rank)
+        got = run.layout_host()
+        assert np.array_equal(got["send"], rt.send) and np.array_equal(got["recv"], rt.recv)
+    else:
+        check_layout(run, n)
     ref = oracle.forward(n, sh.num_experts, sh.num_local_experts, sh.local_rank, sh.block_m)
     y = run.y_host()
     valid = ~np.isnan(ref["y"])
