@@ -2,7 +2,7 @@
 //
 //   GEMM1 (gate_up): for pool block b of local expert le, G = A W1[le]^T over K = H, with A the pooled
 //     FP8 rows.  Epilogue: h = silu(gate) * up, then per row and 128 columns s = max(amax, 1e-4)/448 and
-//     q = e4m3fn(h / s) into the L2 pool ("Mega-MoE kernel code walkthrough: from Dispatch to WGMMA",
+//     q = e4m3fn(h * (1/s)), with 1/s the fp32 reciprocal, into the L2 pool ("Mega-MoE kernel code walkthrough: from Dispatch to WGMMA",
 //     section 6: the L1 epilogue is SwiGLU then FP8; "MoE fused operators", DeepGEMM part, section 5).
 //   GEMM2 (down): O = L2 W2[le]^T over K = I; epilogue casts to bf16 and scatters row m to
 //     comb[k][shard*T_max + token] from the pool metadata ("DeepGEMM Mega MoE symmetric memory deep
@@ -29,7 +29,12 @@
 // DMA instructions (past the end the last step is loaded again), so the wait count is a constant.  LDS rows are 128 bytes with the 16-byte chunks
 // XOR-swizzled by row; the DMA lanes fetch the global chunk that belongs at their LDS position.
 // Tiles map XCD-aware: consecutive work-groups of one XCD take neighbouring tiles of one expert (a few
-// n tiles of all its pool blocks), which share A and B through that XCD's L2.
+// n tiles of all its pool blocks), which share A and B through that XCD's L2.  A stream-ordered launch
+// looks up its work-group's tiles (block, n tile, expert) once, into an LDS table.
+//
+// The same pipeline also runs with MXFP4 weights (kFp4: e2m1 codes with UE8M0 exponents applied by the
+// scaled MFMA) and BF16 tokens and weights (kBf16: two 16x16x32 bf16 MFMAs per fragment pair, no scales,
+// no promotion, and a bf16 L2 pool).
 #include <type_traits>
 
 #include "mm_internal.h"
