@@ -457,9 +457,9 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     // kind of word from wave-uniform bases instead (one more DMA per step, two more with GEMM2).
     constexpr bool kLaneSmall = kWait == kWaitNone;
     // per step: A and B chunks, the small DMA, (MXFP4) the wave's weight-row exponents and (kWait) the
-    // probe of the next tile's word
-    constexpr int DMA_PER_STEP = A_INS + B_INS + 1 + (kFp4 ? 1 : 0) +
-                                 (kLaneSmall ? 0 : (kFp4 ? 0 : 1) + (kGemm1 ? 0 : 1) + 1);
+    // probe of the next tile's word.  BF16 has no scales: with kWait only the targets and the probe.
+    constexpr int DMA_PER_STEP = A_INS + B_INS + (kBf16 && !kLaneSmall ? 0 : 1) + (kFp4 ? 1 : 0) +
+                                 (kLaneSmall ? 0 : (kFp4 || kBf16 ? 0 : 1) + (kGemm1 ? 0 : 1) + 1);
     // global stores every wave issues in a GEMM2 tile's epilogue: two per 16-token group
     constexpr int kEpiStores = 2 * TM;
     // K-start rotation per block within the expert and per n tile (see the issue side below); it
@@ -470,8 +470,9 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
     static_assert(TM * 32 == BM && WN * 16 == WROWS, "tile shape");
     static_assert(kGemm1 || kWait != kWaitFill, "the fill feeds GEMM1 only");
     static_assert(kGemm1 || !kPublish, "GEMM1 publishes its tiles");
-    // BF16 x BF16: stream-ordered tiles only; no scales, K steps of 64 values (128 bytes like FP8)
-    static_assert(!kBf16 || (!kFp4 && kWait == kWaitNone && !kPublish && !kXcd), "BF16 schedule");
+    // BF16 x BF16: no scales, K steps of 64 values (128 bytes like FP8); stream-ordered tiles, or both
+    // GEMMs in one launch (no pull inside it)
+    static_assert(!kBf16 || (!kFp4 && kWait != kWaitFill), "BF16 schedule");
     constexpr int kStages = GemmLds<BM, NW, kFp4>::kStages;
     constexpr int kInFlight = (kStages - 2) * DMA_PER_STEP;   // at mid-step: the steps after the next one
     static_assert((kStages - 1) * DMA_PER_STEP + kEpiStores < 64, "vmcnt immediate");
@@ -677,6 +678,7 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
             iWs = static_cast<const uint8_t*>(sgpr_ptr(reinterpret_cast<const uint8_t*>(kGemm1 ? p.w1_sf : p.w2_sf) +
                                                        (((size_t)le * nts + nt) * KB + ikc) * 1024));
         }
+        // (BF16: no scales; these addresses are formed but never loaded)
         iSc = static_cast<const uint8_t*>(
             sgpr_ptr((kGemm1 ? p.pool_sf : p.l2_sf) + ((size_t)b * KB + ikc) * BM));
         if constexpr (!kFp4) {
@@ -703,8 +705,10 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
             dma4_lane(iSm, &sSmall[buf][wave * 64]);
             if constexpr (kFp4) dma4_lane(iWsl, &sWs[buf][wave * 64]);
         } else {
-            if (sc_lane) dma4(iSc, sm_off, &sSmall[buf][wave * 64]);
-            if constexpr (!kFp4) {
+            if constexpr (!kBf16) {
+                if (sc_lane) dma4(iSc, sm_off, &sSmall[buf][wave * 64]);
+            }
+            if constexpr (!kFp4 && !kBf16) {
                 if (ws_lane) dma4(iWsc, sm_off, &sSmall[buf][wave * 64]);
             }
             if constexpr (!kGemm1) {
@@ -888,6 +892,11 @@ __device__ __forceinline__ void gemm_phase(const Params& p, const TilePlan& plan
                 if (g == 0) sRed[wm * (BM / 2) + t * 16 + rr][wn] = m;
             }
             if constexpr (kBf16) {
+                if constexpr (kPublish) {
+                    // as below: the tile's stores have completed, then one lane counts the tile
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                    if (wave == 0 && lane == 0) atomicAdd(p.sched + kSchedArrival + p.max_blocks + b, 1u);
+                }
 #pragma unroll
                 for (int a = 0; a < WN; ++a)
 #pragma unroll
@@ -1154,8 +1163,9 @@ __device__ __forceinline__ bool route_in_launch(const Params& p, int tid) {
 
 // Launch whose work-groups hand rows over by XCD (see the top of this section): [route (kRoute),] [pull
 // the pool rows (kFill),] GEMM1 [, then GEMM2 (kBoth)] over the pool blocks of the work-group's XCD.
-template <int BM, int NW, bool kFill, bool kBoth, bool kStreamW, bool kFp4, bool kRoute = false>
+template <int BM, int NW, bool kFill, bool kBoth, bool kStreamW, bool kFp4, bool kRoute = false, bool kBf16 = false>
 __global__ __launch_bounds__(NW * 64, 1) void xcd_gemm_kernel(Params p) {
+    static_assert(!kBf16 || (kBoth && !kFill && !kRoute), "BF16: both GEMMs in one launch, no pull inside it");
     const int tid = threadIdx.x, lane = tid & 63;
     if constexpr (kRoute) {
         if (!route_in_launch<BM, NW, kFp4>(p, tid)) {
@@ -1214,9 +1224,9 @@ __global__ __launch_bounds__(NW * 64, 1) void xcd_gemm_kernel(Params p) {
             auto pk = (const __attribute__((address_space(4))) Params*)__builtin_amdgcn_kernarg_segment_ptr();
             asm volatile("" : "+s"(pk));
             const Params q = *(const Params*)pk;
-            gemm_phase<BM, NW, true, kStreamW, kFp4, kFill ? kWaitFill : kWaitNone, true, true>(q, wave, nblocks);
+            gemm_phase<BM, NW, true, kStreamW, kFp4, kFill ? kWaitFill : kWaitNone, true, true, kBf16>(q, wave, nblocks);
             __syncthreads();
-            gemm_phase<BM, NW, false, kStreamW, kFp4, kWaitGemm1, false, true>(q, wave, nblocks);
+            gemm_phase<BM, NW, false, kStreamW, kFp4, kWaitGemm1, false, true, kBf16>(q, wave, nblocks);
             __syncthreads();
         }
     } else {
@@ -1233,11 +1243,11 @@ hipError_t launch(const Params& p, int num_cus, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int BM, bool kFill, bool kBoth, bool kStreamW = false, bool kFp4 = false>
+template <int BM, bool kFill, bool kBoth, bool kStreamW = false, bool kFp4 = false, bool kBf16 = false>
 hipError_t launch_xcd(const Params& p, int num_cus, hipStream_t stream) {
     const int grid = (num_cus + 7) / 8 * 8;
     if (grid / kXcds > 32) return hipErrorInvalidConfiguration;     // one slot word per XCD
-    hipLaunchKernelGGL((xcd_gemm_kernel<BM, kWaves, kFill, kBoth, kStreamW, kFp4>), dim3(grid),
+    hipLaunchKernelGGL((xcd_gemm_kernel<BM, kWaves, kFill, kBoth, kStreamW, kFp4, false, kBf16>), dim3(grid),
                        dim3(kWaves * 64), 0, stream, p);
     return hipGetLastError();
 }
@@ -1304,6 +1314,13 @@ hipError_t launch_route_fill_gemms(const Params& p, int num_cus, hipStream_t str
 
 hipError_t launch_gemms(const Params& p, bool fuse_fill, int num_cus, hipStream_t stream) {
     const bool sw = p.BM == 64 && weights_stream(p);
+    if (p.wfmt == MEGA_MOE_WEIGHTS_BF16) {
+        if (fuse_fill) return hipErrorInvalidConfiguration;   // (refused by the config check)
+        if (p.BM == 64)
+            return sw ? launch_xcd<64, false, true, true, false, true>(p, num_cus, stream)
+                      : launch_xcd<64, false, true, false, false, true>(p, num_cus, stream);
+        return launch_xcd<128, false, true, false, false, true>(p, num_cus, stream);
+    }
     if (p.wfmt == MEGA_MOE_WEIGHTS_MXFP4) {
         if (p.BM == 64)
             return sw ? launch_xcd<64, false, true, true, true>(p, num_cus, stream)

@@ -69,9 +69,9 @@ int32_t check_config(const mega_moe_config* c) {
     if (c->weight_format != MEGA_MOE_WEIGHTS_FP8 && c->weight_format != MEGA_MOE_WEIGHTS_MXFP4 &&
         c->weight_format != MEGA_MOE_WEIGHTS_BF16)
         return MEGA_MOE_ERR_UNSUPPORTED;
-    // BF16 x BF16 runs the stream-ordered kernels only
+    // BF16 x BF16: stream-ordered kernels, or both GEMMs in one launch (no pull inside it)
     if (c->weight_format == MEGA_MOE_WEIGHTS_BF16 &&
-        (c->flags & (MEGA_MOE_FLAG_FILL_IN_GEMM1 | MEGA_MOE_FLAG_ONE_GEMM_LAUNCH | MEGA_MOE_FLAG_ROUTE_IN_LAUNCH)))
+        (c->flags & (MEGA_MOE_FLAG_FILL_IN_GEMM1 | MEGA_MOE_FLAG_ROUTE_IN_LAUNCH)))
         return MEGA_MOE_ERR_UNSUPPORTED;
     // the arrival-counted fill (and the launch that also routes) is built for FP8 weights only
     if (c->weight_format == MEGA_MOE_WEIGHTS_MXFP4 &&

@@ -121,8 +121,9 @@ extern "C" {
                                     /* kernel the pages select by operand type, whose input buffer takes */
                                     /* the tokens without scale factors ("DeepGEMM Mega MoE symmetric    */
                                     /* memory deep analysis", 5.3 and 10.1).  The pool, the L2 pool and  */
-                                    /* GEMM1's output (SwiGLU rounded to bf16) hold bf16 values.  Stream-*/
-                                    /* ordered kernels only: the in-launch schedule flags are refused   */
+                                    /* GEMM1's output (SwiGLU rounded to bf16) hold bf16 values.  With  */
+                                    /* ONE_GEMM_LAUNCH or stream-ordered kernels; FILL_IN_GEMM1 and     */
+                                    /* ROUTE_IN_LAUNCH are refused (the in-launch pull is FP8's)         */
 
 /* Stage bits for mega_moe_forward_stages.  mega_moe_forward runs all of them, in this order. */
 #define MEGA_MOE_STAGE_ROUTE 0x1u     /* counts, table, pool offsets, block list, pool row metadata and */

@@ -155,21 +155,23 @@ def test_shared_expert_config_and_workspace():
 
 
 def test_weight_format_config():
-    """MXFP4 and BF16 weights are config values (MXFP4 with or without the one-launch GEMMs); other
-    values, the arrival-counted fill with MXFP4, and every in-launch schedule with BF16 are rejected."""
+    """MXFP4 and BF16 weights are config values (either with or without the one-launch GEMMs); other
+    values, and the in-launch pull (arrival-counted fill, routing in the launch) with MXFP4 or BF16
+    weights, are rejected."""
     import ctypes
     lib = mm.lib()
     out = ctypes.c_uint64(0)
     for ok in (cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4),
                cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_ONE_GEMM_LAUNCH),
                cfg_of("decode", flags=mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_FILL_IN_GEMM1),
-               cfg_of("decode", weight_format=mm.WEIGHTS_BF16)):
+               cfg_of("decode", weight_format=mm.WEIGHTS_BF16),
+               cfg_of("decode", weight_format=mm.WEIGHTS_BF16, flags=mm.FLAG_ONE_GEMM_LAUNCH)):
         assert lib.mega_moe_workspace_bytes(ctypes.byref(ok), ctypes.byref(out)) == mm.OK
     for c in (cfg_of("decode", weight_format=3), cfg_of("decode", weight_format=-1),
               cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_FILL_IN_GEMM1),
               cfg_of("decode", weight_format=mm.WEIGHTS_MXFP4, flags=mm.FLAG_ROUTE_IN_LAUNCH),
               cfg_of("decode", weight_format=mm.WEIGHTS_BF16, flags=mm.FLAG_FILL_IN_GEMM1),
-              cfg_of("decode", weight_format=mm.WEIGHTS_BF16, flags=mm.FLAG_ONE_GEMM_LAUNCH),
+              cfg_of("decode", weight_format=mm.WEIGHTS_BF16, flags=mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_FILL_IN_GEMM1),
               cfg_of("decode", weight_format=mm.WEIGHTS_BF16, flags=mm.FLAG_ROUTE_IN_LAUNCH)):
         assert lib.mega_moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == mm.ERR_UNSUPPORTED
 

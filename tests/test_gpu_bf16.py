@@ -272,3 +272,54 @@ def test_bf16_random_configs_whole_layer(case):
     _check_layout_bf16(run, n)
     _whole(run, n)
     run.close()
+
+
+def _sched_words(moe):
+    n = 64 + 2 * moe.layout["max_pool_blocks"]
+    return moe.region("sched", torch.int32, (n,)).cpu().numpy()
+
+
+def _one_launch_matches(sh, tps):
+    inp = make_inputs(sh, device="cuda", tokens_per_shard=tps)
+    base = mm.MegaMoE.from_shape(sh)
+    want = base(inp)
+    torch.cuda.synchronize()
+    assert base.status() == 0
+    nb = int(base.region("status", torch.int32, (2,))[1].item())
+    L = base.layout
+    l2_want = base.region("l2_x", torch.int16, (L["max_pool_blocks"], sh.intermediate * base.block_m))[:nb].clone()
+    moe = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_ONE_GEMM_LAUNCH)
+    for _ in range(2):
+        got = moe(inp)
+        torch.cuda.synchronize()
+        assert moe.status() == 0
+        assert not _sched_words(moe).any(), "schedule words left non-zero"
+        l2 = moe.region("l2_x", torch.int16, (L["max_pool_blocks"], sh.intermediate * moe.block_m))[:nb]
+        assert torch.equal(l2, l2_want), "L2 pool"
+        for i, n in enumerate(tps):
+            assert torch.equal(got[i, :n].view(torch.int16), want[i, :n].view(torch.int16)), i
+    moe.close()
+    base.close()
+
+
+@pytest.mark.parametrize("case", ["bm64_ragged", "bm128_waves"])
+def test_bf16_one_gemm_launch_matches_stream_order(case):
+    """Both BF16 GEMMs in one persistent launch (each GEMM2 tile waits on its block's count of finished
+    GEMM1 n tiles, in expert waves per XCD): the L2 pool and the output bit for bit as the stream-ordered
+    kernels give them, twice in a row, with a clean status and every schedule word back at zero."""
+    print(f"[case] bf16 one GEMM launch {case}", flush=True)
+    if case == "bm64_ragged":
+        sh = MoEShape("bf1l64", 5, 333, 1024, 256, 64, 16, 6, 64, local_rank=1, weight_format="bf16", seed=211)
+        tps = [333, 0, 101, 7, 250]
+    else:
+        sh = MoEShape("bf1lw", 4, 1024, 512, 1024, 128, 64, 8, 128, local_rank=1, weight_format="bf16", seed=212)
+        tps = [1024, 1000, 777, 1024]
+    _one_launch_matches(sh, tps)
+
+
+@pytest.mark.parametrize("case", range(len(_BF16_SWEEP)), ids=[sh.name for sh, _ in _BF16_SWEEP])
+def test_bf16_random_configs_one_gemm_launch(case):
+    """The seeded BF16 configurations with both GEMMs in one launch: bits equal to stream order."""
+    sh, tps = _BF16_SWEEP[case]
+    print(f"[case] bf16 one GEMM launch {sh.name} tps={tps}", flush=True)
+    _one_launch_matches(sh, tps)
