@@ -323,3 +323,25 @@ def test_bf16_random_configs_one_gemm_launch(case):
     sh, tps = _BF16_SWEEP[case]
     print(f"[case] bf16 one GEMM launch {sh.name} tps={tps}", flush=True)
     _one_launch_matches(sh, tps)
+
+
+def test_bf16_one_gemm_launch_forced_timeout_latches_and_recovers():
+    """BF16 weights with both GEMMs in one launch, its bounded GEMM2 waits forced from the host to give
+    up at once: the status word reports TIMEOUT, the launch completes and zeroes its schedule words,
+    and a normal handle on the same inputs then matches the oracle."""
+    print("[case] bf16 one GEMM launch, forced wait timeout", flush=True)
+    sh = MoEShape("bftmo", 2, 80, 256, 128, 8, 4, 2, 64, weight_format="bf16", seed=213)
+    inp = make_inputs(sh, device="cuda")
+    forced = mm.MegaMoE.from_shape(sh, flags=mm.FLAG_ONE_GEMM_LAUNCH | mm.FLAG_DEBUG_FORCE_TIMEOUT)
+    for _ in range(2):
+        forced(inp)
+        torch.cuda.synchronize()
+        assert forced.status() == mm.STATUS_TIMEOUT
+        assert not _sched_words(forced).any()
+    forced.close()
+    run = Run(sh, inputs=inp, flags=mm.FLAG_ONE_GEMM_LAUNCH)
+    assert run.status == 0
+    n = inputs_np(run)
+    _check_layout_bf16(run, n)
+    _whole(run, n)
+    run.close()
