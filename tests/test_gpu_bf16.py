@@ -184,12 +184,15 @@ def test_bf16_repeat_and_poisoned_workspace_identical():
     inp = make_inputs(sh, tokens_per_shard=tps)
     clean = Run(sh, inputs=inp, repeat=2)
     pois = Run(sh, inputs=inp, flags=mm.FLAG_DEBUG_POISON, repeat=2)
-    assert clean.status == 0 and pois.status == 0
-    for y in clean.ys + pois.ys:
+    # both GEMMs in one launch over a poisoned workspace: a GEMM2 load overtaking GEMM1's stores would show
+    pois1 = Run(sh, inputs=inp, flags=mm.FLAG_DEBUG_POISON | mm.FLAG_ONE_GEMM_LAUNCH, repeat=2)
+    assert clean.status == 0 and pois.status == 0 and pois1.status == 0
+    for y in clean.ys + pois.ys + pois1.ys:
         for i, cnt in enumerate(tps):
             assert torch.equal(y[i, :cnt].view(torch.int16), clean.ys[0][i, :cnt].view(torch.int16))
     clean.close()
     pois.close()
+    pois1.close()
 
 
 def test_bf16_full_size_decode_sampled_tokens():
