@@ -273,6 +273,25 @@ def test_requant_uses_the_fp32_reciprocal_of_the_scale():
     assert oracle.e4m3fn_decode(oracle.e4m3fn_encode(np.float32(h[0, 1] / s[0, 0])[None]))[0] == 416.0
 
 
+def test_requant_scale_granularity():
+    """The scale covers `gran` columns: a row of two 64-column halves holding 1.0 and 4.0 gets, with
+    gran = 64, scales 1/448 and 4/448 and every code 448 (e4m3fn 0x7E); with gran = 128, the one scale
+    4/448, codes 448 for the second half and 448/4 = 112 (0x6E: 2^6 * 1.75) for the first."""
+    h = np.concatenate([np.full((1, 64), 1.0), np.full((1, 64), 4.0)], axis=1)
+    q, s = oracle.requant_rows(h, gran=64)
+    assert s.shape == (1, 2)
+    assert s[0, 0] == np.float32(np.float32(1.0) / np.float32(448))
+    assert s[0, 1] == np.float32(np.float32(4.0) / np.float32(448))
+    assert np.all(q == 0x7E)
+    q, s = oracle.requant_rows(h)
+    assert s.shape == (1, 1) and s[0, 0] == np.float32(np.float32(4.0) / np.float32(448))
+    assert np.all(q[0, :64] == 0x6E) and np.all(q[0, 64:] == 0x7E)
+    # each half comes back from its own code and scale
+    q, s = oracle.requant_rows(h, gran=64)
+    back = oracle.e4m3fn_decode(q) * np.repeat(s.astype(np.float64), 64, axis=1)
+    assert np.allclose(back, h, rtol=1e-6, atol=0)
+
+
 def test_gemm1_exact_on_integer_codes():
     """Integer codes with power-of-two scales: G equals an int64 matmul times the scales."""
     sh = MoEShape("t", 1, 32, 256, 128, 2, 2, 1, 64)
