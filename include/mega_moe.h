@@ -79,7 +79,8 @@ extern "C" {
                                                   tile waits on its block's count instead of a kernel
                                                   boundary.  Each XCD pulls and computes its own range of
                                                   pool blocks, so the hand-over stays in its L2.  Same
-                                                  results bit for bit */
+                                                  results bit for bit.  FP8 weights only (the config
+                                                  check refuses it with MXFP4 or BF16 weights) */
 #define MEGA_MOE_FLAG_DEBUG_FORCE_TIMEOUT 0x4u /* tests: with FILL_IN_GEMM1 or ONE_GEMM_LAUNCH, every bounded
                                                   wait gives up at once and latches MEGA_MOE_STATUS_TIMEOUT
                                                   (the kernel still exits normally and zeroes its schedule
